@@ -1,0 +1,264 @@
+"""Benchmark of the k8v4 decode step on one MI355X.
+
+One step = one decode step of one layer at 64K context: quantize-and-append
+the new token's key/value (32 query / 8 kv heads, D 128, bf16) and attend the
+65536 cached tokens with the single bf16 query token.  Steps rotate over
+distinct layer caches whose total size exceeds 4 x 256 MiB (the MI355X
+last-level cache), so every step streams its cache from HBM.
+
+Prints one JSON line.  ``value`` is the achieved algorithmic HBM bandwidth of
+the whole step (GB/s); ``tok_s_per_layer`` is query tokens per second per
+layer; ``roofline`` reports the attention kernel alone, timed with HIP events
+on the stream it runs on.  ``cpu_baseline`` times the CPU oracle on the same
+workload (a bounded number of steps).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20
+
+
+def cache_bytes_per_token_head(D: int) -> int:
+    # key codes D + key scale 2 + value codes D/2 + value scales 2*D/32
+    return D + 2 + D // 2 + 2 * (D // 32)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa_decode_65536",
+                    choices=["gqa_decode_65536", "gqa_decode_4096", "verify_65536_w8", "multi_session_16x32768"])
+    ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0: enough for 4x LLC)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--tune", action="store_true", help="run tune_select first and use its choice")
+    ap.add_argument("--config", default="", help="JSON dict of launch config fields")
+    ap.add_argument("--kernel-only", action="store_true", help="time only the attention launches (profiling)")
+    ap.add_argument("--contiguous-pages", action="store_true", help="identity page table (profiling)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the sharding design is described in DESIGN.md)"}))
+        return 2
+    import torch
+
+    import decode_attention_quantized_kv_amd as q8
+    import workloads
+
+    q8.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = workloads.NAMED[args.workload]()
+    if args.contiguous_pages:
+        # relabel physical pages so that sequence 0's pages are in logical order
+        perm = np.argsort(w.page_table[0][: (int(w.seq_lens[0]) + 15) // 16])
+        full = np.arange(w.num_pages)
+        full[: len(perm)] = perm
+        relabel = lambda t: full[t].astype(np.int32)
+        w.page_table = relabel(w.page_table)
+        for a in w.appends:
+            a.page_table = relabel(a.page_table)
+    Hq, H, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    per_th = cache_bytes_per_token_head(D)
+    unique = w.unique_tokens()
+    layer_bytes = w.num_pages * H * 16 * per_th
+    layers = args.layers or max(2, -(-4 * LLC_BYTES // layer_bytes) + 1)
+
+    def to_dev(a, bf=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if bf:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    bf = w.dtype == "bf16"
+    caches = [q8.PagedKVCache(w.num_pages, H, D) for _ in range(layers)]
+    batches = [(to_dev(a.k, bf), to_dev(a.v, bf), to_dev(a.cu_new), to_dev(a.start_pos), to_dev(a.page_table))
+               for a in w.appends]
+    for c in caches:
+        for (k, v, cu, sp, pt) in batches:
+            q8.kv_quant_append(c, k, v, cu, sp, pt)
+    torch.cuda.synchronize()
+    # the step's new token: the last cached token of every sequence, re-appended
+    last = w.appends[-1]
+    B = w.n_seqs
+    rows = (last.cu_new[1:] - 1).astype(np.int64)
+    step_k = to_dev(last.k[rows], bf)
+    step_v = to_dev(last.v[rows], bf)
+    step_cu = to_dev(np.arange(B + 1, dtype=np.int32))
+    step_pos = to_dev((w.seq_lens - 1).astype(np.int32))
+    page_table = to_dev(w.page_table)
+    seq_lens = to_dev(w.seq_lens)
+    q = to_dev(w.q, bf)
+    msl = int(w.seq_lens.max())
+    cfg = q8.make_config(**json.loads(args.config)) if args.config else None
+    tuned = None
+    if args.tune:
+        dcfg, vcfg, rep = q8.tune_select(Hq, H, D, n_draft=max(1, w.n_draft or 8), install=True)
+        cfg = vcfg if w.n_draft else dcfg
+        tuned = cfg.as_dict()
+    nd = w.n_draft
+    ws = torch.zeros(max(16, q8.workspace_bytes(B, Hq, H, D, msl, nd, cfg)), dtype=torch.uint8, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def attend(c):
+        if nd:
+            q8.attn_verify_q8k4v(c, q, seq_lens, msl, page_table, w.softmax_scale, out=out, cfg=cfg, workspace=ws)
+        else:
+            q8.attn_decode_q8k4v(c, q, seq_lens, msl, page_table, w.softmax_scale, out=out, cfg=cfg, workspace=ws)
+
+    def step(i):
+        c = caches[i % layers]
+        q8.kv_quant_append(c, step_k, step_v, step_cu, step_pos, page_table, total_new=B)
+        attend(c)
+
+    # Steps are captured in HIP graphs (one graph = one pass over all layer
+    # caches) so that the timing sees device work, not host launch overhead.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(layers):
+                fn(i)
+        return g
+
+    def timed(g, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * layers)
+
+    # eager reference of the last layer, then every graph replay must match it
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    attend(caches[layers - 1])
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    step_graph = capture(step)
+    attn_graph = capture(lambda i: attend(caches[i]))
+    reps = max(1, -(-args.steps // layers))
+    for g in (step_graph, attn_graph):
+        for _ in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref_out):
+                raise RuntimeError("graph replay differs from the eager result")
+            attend(caches[layers - 1])          # eager work between replays
+            torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = timed(attn_graph if args.kernel_only else step_graph, reps)
+    wall = time.perf_counter() - t0
+    ms_attn = timed(attn_graph, reps)
+    args.steps = reps * layers
+
+    q_bytes = q.numel() * q.element_size()
+    o_bytes = out.numel() * 4
+    attn_bytes = unique * H * per_th + q_bytes + o_bytes
+    elem = 2 if bf else 4
+    append_bytes = B * H * D * 2 * elem + B * H * per_th
+    step_bytes = attn_bytes + (0 if args.kernel_only else append_bytes)
+    tokens = B * max(1, nd)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = attn_bytes / (ms_attn * 1e-3) / 1e9
+
+    res = {
+        "metric": "achieved HBM GB/s (% of peak) + decode tok/s/layer, q8K/q4V attn at 64K ctx",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tok_s_per_layer": round(tokens / (ms_step * 1e-3), 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, int8 K / int4 V codes, fp16 MACs, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1), 1% outlier channels x8, bf16), random page permutation",
+        "config": {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": H, "head_dim": D,
+                   "context": int(w.seq_lens.max()), "n_seqs": B, "n_draft": nd, "page_size": 16,
+                   "rotating_layer_caches": layers, "layer_cache_bytes": layer_bytes,
+                   "launch_config": tuned or (cfg.as_dict() if cfg else "default")},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attention (split-K attention kernel + combine)", "algorithmic_bytes": attn_bytes,
+                     "avg_launch_us": round(ms_attn * 1e3, 3)},
+        "step_bytes": step_bytes,
+        "wall_s": round(wall, 3),
+        "device": device_info(torch),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_steps, step_bytes, tokens)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def device_info(torch) -> dict:
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "mem_gib": round(p.total_memory / 2**30, 1)}
+
+
+def cpu_baseline(w, steps: int, step_bytes: int, tokens: int) -> dict:
+    """The CPU oracle as it stands, on this host: one step = quantize-append
+    the new token + fp64 attention over the dequantized cache."""
+    from oracle import attention, codec
+    cache = codec.PagedCache(w.num_pages, w.num_kv_heads, w.head_dim)
+    for a in w.appends:
+        codec.append(cache, a.k, a.v, w.dtype, a.cu_new, a.start_pos, a.page_table)
+    last = w.appends[-1]
+    B = w.n_seqs
+    rows = (last.cu_new[1:] - 1).astype(np.int64)
+    times = []
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        codec.append(cache, last.k[rows], last.v[rows], w.dtype, np.arange(B + 1, dtype=np.int32),
+                     (w.seq_lens - 1).astype(np.int32), w.page_table)
+        if w.n_draft:
+            attention.verify(cache, w.q, w.dtype, w.page_table, w.seq_lens, w.softmax_scale)
+        else:
+            attention.decode(cache, w.q, w.dtype, w.page_table, w.seq_lens, w.softmax_scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        pass
+    return {"value": round(step_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads or 1,
+            "kind": "oracle", "s_per_step": round(t, 3), "tok_s_per_layer": round(tokens / t, 4),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{steps} full steps of {w.name} (median); numpy elementwise work is single-threaded, "
+                      f"matmuls use the BLAS pool"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,277 @@
+"""Python binding of the gfx950 k8v4 attention library (``libq8k4v.so``).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: importing works without the library, but every call raises if it is
+not built or cannot be loaded.
+
+Entry points (same names as the C ABI in ``include/q8k4v.h``):
+``kv_quant_append``, ``attn_decode_q8k4v``, ``attn_verify_q8k4v``,
+``tune_select``; plus ``workspace_bytes`` and ``PagedKVCache`` (allocates the
+four cache pools as torch tensors).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import json
+import math
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libq8k4v.so")
+
+Q8K4V_OK = 0
+F32, BF16 = 0, 1
+PAGE_SIZE = 16
+MAX_DRAFT = 16
+
+ERRORS = {-1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "ENOMEM"}
+
+
+class Q8K4VError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {ERRORS.get(code, code)} ({msg})")
+        self.code = code
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("num_pages", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_size", C.c_int32), ("k_codes", C.c_void_p), ("k_scales", C.c_void_p),
+                ("v_codes", C.c_void_p), ("v_scales", C.c_void_p)]
+
+
+class Config(C.Structure):
+    _fields_ = [("wgs_per_cu", C.c_int32), ("split_pages", C.c_int32), ("tile_pages", C.c_int32),
+                ("waves_per_wg", C.c_int32), ("fused_combine", C.c_int32), ("qualified", C.c_int32),
+                ("variant", C.c_int32), ("reserved", C.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class TuneRequest(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("n_draft", C.c_int32), ("ctx_small", C.c_int32), ("ctx_large", C.c_int32),
+                ("budget_ms", C.c_int64), ("mem_cap_bytes", C.c_size_t), ("seed", C.c_uint64),
+                ("install", C.c_int32), ("max_candidates", C.c_int32),
+                ("ref_cache", C.POINTER(CacheDesc)), ("ref_q", C.c_void_p), ("ref_q_verify", C.c_void_p),
+                ("ref_page_table", C.c_void_p), ("ref_len", C.c_int32), ("ref_max_pages", C.c_int32),
+                ("ref_out", C.c_void_p), ("ref_out_verify", C.c_void_p), ("ref_tol", C.c_float),
+                ("softmax_scale", C.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> C.CDLL:
+    """Load ``libq8k4v.so`` (raises if it is missing: build it with
+    ``python -m decode_attention_quantized_kv_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run python -m decode_attention_quantized_kv_amd.build)")
+    lib = C.CDLL(path)
+    i32, vp, sz = C.c_int32, C.c_void_p, C.c_size_t
+    lib.q8k4v_last_error.restype = C.c_char_p
+    lib.q8k4v_version.restype = C.c_char_p
+    lib.kv_quant_append.restype = i32
+    lib.kv_quant_append.argtypes = [C.POINTER(CacheDesc), vp, vp, i32, vp, vp, vp, i32, i32, i32, vp]
+    lib.q8k4v_workspace_bytes.restype = sz
+    lib.q8k4v_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(Config)]
+    lib.attn_decode_q8k4v.restype = i32
+    lib.attn_decode_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, vp, i32, vp, i32,
+                                      C.c_float, C.POINTER(Config), vp, sz, vp]
+    lib.attn_verify_q8k4v.restype = i32
+    lib.attn_verify_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, i32, vp, i32, vp, i32,
+                                      C.c_float, C.POINTER(Config), vp, sz, vp]
+    lib.tune_select.restype = i32
+    lib.tune_select.argtypes = [C.POINTER(TuneRequest), C.POINTER(Config), C.c_char_p, sz]
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().q8k4v_version().decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != Q8K4V_OK:
+        raise Q8K4VError(fn, rc, load_library().q8k4v_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> C.c_void_p:
+    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def make_config(**kw) -> Config:
+    c = Config()
+    for k, v in kw.items():
+        setattr(c, k, int(v))
+    return c
+
+
+class PagedKVCache:
+    """The four device pools of a paged k8v4 cache (torch tensors), in the
+    library's layout:
+
+    ``k_codes [P][H][16][D] int8``, ``k_scales [P][H][16]`` fp16 bits,
+    ``v_codes [P][H][D][8] uint8``, ``v_scales [P][H][16][D/32]`` fp16 bits."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda"):
+        torch = _torch()
+        P, H, D = num_pages, num_kv_heads, head_dim
+        self.num_pages, self.num_kv_heads, self.head_dim = P, H, D
+        self.k_codes = torch.zeros((P, H, PAGE_SIZE, D), dtype=torch.int8, device=device)
+        self.k_scales = torch.zeros((P, H, PAGE_SIZE), dtype=torch.int16, device=device)
+        self.v_codes = torch.zeros((P, H, D, PAGE_SIZE // 2), dtype=torch.uint8, device=device)
+        self.v_scales = torch.zeros((P, H, PAGE_SIZE, D // 32), dtype=torch.int16, device=device)
+        self._desc = None
+
+    @property
+    def desc(self) -> CacheDesc:
+        if self._desc is None:
+            self._desc = CacheDesc(self.num_pages, self.num_kv_heads, self.head_dim, PAGE_SIZE,
+                                   self.k_codes.data_ptr(), self.k_scales.data_ptr(),
+                                   self.v_codes.data_ptr(), self.v_scales.data_ptr())
+        return self._desc
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+
+
+def kv_quant_append(cache: PagedKVCache, k_new, v_new, cu_new, start_pos, page_table,
+                    total_new: Optional[int] = None, stream=None) -> None:
+    """``k_new``/``v_new``: ``[N][H][D]`` float32 or bfloat16 (device);
+    ``cu_new [B+1]``, ``start_pos [B]``, ``page_table [B][max_pages]`` int32
+    (device)."""
+    lib = load_library()
+    if total_new is None:
+        total_new = int(k_new.shape[0])
+    n_seqs = int(start_pos.shape[0])
+    rc = lib.kv_quant_append(C.byref(cache.desc), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(cu_new),
+                             _ptr(start_pos), _ptr(page_table), int(page_table.shape[1]), n_seqs,
+                             int(total_new), _stream(stream))
+    _check("kv_quant_append", rc)
+
+
+def workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_seq_len: int,
+                    n_draft: int = 0, cfg: Optional[Config] = None) -> int:
+    lib = load_library()
+    return int(lib.q8k4v_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, n_draft,
+                                         C.byref(cfg) if cfg is not None else None))
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def attn_decode_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_table,
+                      softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
+                      workspace=None, stream=None):
+    """``q [B][Hq][D]`` (float32/bfloat16, device) -> ``out [B][Hq][D]`` float32."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, 0, cfg), q.device)
+    rc = lib.attn_decode_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq, _ptr(seq_lens),
+                               int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+                               float(softmax_scale), C.byref(cfg) if cfg is not None else None,
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("attn_decode_q8k4v", rc)
+    return out
+
+
+def attn_verify_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_table,
+                      softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
+                      workspace=None, stream=None):
+    """``q [B][W][Hq][D]`` -> ``out [B][W][Hq][D]`` float32; draft j of
+    sequence b sees positions ``0 .. seq_lens[b] - W + j``."""
+    torch = _torch()
+    lib = load_library()
+    B, Wd, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Wd, Hq, D), dtype=torch.float32, device=q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, Wd, cfg), q.device)
+    rc = lib.attn_verify_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq, Wd,
+                               _ptr(seq_lens), int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+                               float(softmax_scale), C.byref(cfg) if cfg is not None else None,
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("attn_verify_q8k4v", rc)
+    return out
+
+
+def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int = 8,
+                ctx_small: int = 4096, ctx_large: int = 65536, budget_ms: int = 60000,
+                mem_cap_bytes: int = 0, seed: int = 0, install: bool = False, max_candidates: int = 0,
+                ref=None, report_cap: int = 1 << 20):
+    """Runs the on-device tuner.  ``ref`` (optional) is a dict with keys
+    ``cache`` (PagedKVCache), ``q``, ``q_verify``, ``page_table`` (device),
+    ``length``, ``out``, ``out_verify`` (host float32 numpy) and ``tol``.
+    Returns (decode Config, verify Config, report dict)."""
+    lib = load_library()
+    req = TuneRequest()
+    req.num_q_heads, req.num_kv_heads, req.head_dim, req.n_draft = num_q_heads, num_kv_heads, head_dim, n_draft
+    req.ctx_small, req.ctx_large, req.budget_ms = ctx_small, ctx_large, budget_ms
+    req.mem_cap_bytes, req.seed, req.install, req.max_candidates = mem_cap_bytes, seed, int(install), max_candidates
+    keep = []
+    if ref is not None:
+        import numpy as np
+        out = np.ascontiguousarray(ref["out"], dtype=np.float32)
+        outv = np.ascontiguousarray(ref["out_verify"], dtype=np.float32)
+        keep += [out, outv]
+        req.ref_cache = C.pointer(ref["cache"].desc)
+        req.ref_q = ref["q"].data_ptr()
+        req.ref_q_verify = ref["q_verify"].data_ptr()
+        req.ref_page_table = ref["page_table"].data_ptr()
+        req.ref_len = int(ref["length"])
+        req.ref_max_pages = int(ref["page_table"].numel())
+        req.ref_out = out.ctypes.data
+        req.ref_out_verify = outv.ctypes.data
+        req.ref_tol = float(ref["tol"])
+    table = (Config * 2)()
+    buf = C.create_string_buffer(report_cap)
+    rc = lib.tune_select(C.byref(req), table, buf, report_cap)
+    _check("tune_select", rc)
+    text = buf.value.decode()
+    try:
+        report = json.loads(text) if text else {}
+    except json.JSONDecodeError:
+        report = {"raw": text}
+    return table[0], table[1], report
+
+
+__all__ = ["kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select", "workspace_bytes",
+           "PagedKVCache", "Config", "make_config", "load_library", "version", "Q8K4VError", "LIB_PATH"]

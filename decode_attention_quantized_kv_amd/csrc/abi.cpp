@@ -1,0 +1,320 @@
+// C ABI of the k8v4 attention library: argument validation, launch planning
+// and dispatch.  See include/q8k4v.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attn_common.h"
+#include "q8k4v_internal.h"
+
+#ifndef Q8K4V_BUILD_ID
+#define Q8K4V_BUILD_ID "dev"
+#endif
+
+namespace q8k4v {
+
+int32_t launch_valu(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
+int32_t launch_bmfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
+int32_t launch_mfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
+int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
+
+namespace {
+thread_local std::string g_last_error;
+
+struct TunedEntry {
+    bool mfma;
+    int32_t hq, hkv, d;
+    q8k4v_config cfg;
+};
+std::mutex g_tuned_mu;
+std::vector<TunedEntry> g_tuned;
+
+bool valid_cache(const q8k4v_cache* c, std::string* why) {
+    if (!c) { *why = "cache is NULL"; return false; }
+    if (c->head_dim != 64 && c->head_dim != 128) { *why = "head_dim must be 64 or 128"; return false; }
+    if (c->page_size != Q8K4V_PAGE_SIZE) { *why = "page_size must be 16"; return false; }
+    if (c->num_kv_heads < 1 || c->num_pages < 1) { *why = "num_kv_heads and num_pages must be >= 1"; return false; }
+    if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales) { *why = "a cache pool pointer is NULL"; return false; }
+    return true;
+}
+
+int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+}  // namespace
+
+int32_t fail(int32_t code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+    return fail(Q8K4V_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int32_t device_cu_count() {
+    // compute units of the current device, looked up once per device
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+q8k4v_config default_config(bool mfma) {
+    q8k4v_config c;
+    std::memset(&c, 0, sizeof(c));
+    c.wgs_per_cu = 5;
+    c.split_pages = 0;
+    c.tile_pages = mfma ? 2 : 4;
+    c.waves_per_wg = 2;
+    c.fused_combine = 0;
+    c.qualified = 0;
+    c.variant = 0;
+    return c;
+}
+
+bool tuned_lookup(bool mfma, int32_t hq, int32_t hkv, int32_t d, q8k4v_config* cfg) {
+    std::lock_guard<std::mutex> lk(g_tuned_mu);
+    for (const auto& e : g_tuned)
+        if (e.mfma == mfma && e.hq == hq && e.hkv == hkv && e.d == d) { *cfg = e.cfg; return true; }
+    return false;
+}
+
+void tuned_install(bool mfma, int32_t hq, int32_t hkv, int32_t d, const q8k4v_config& cfg) {
+    std::lock_guard<std::mutex> lk(g_tuned_mu);
+    for (auto& e : g_tuned)
+        if (e.mfma == mfma && e.hq == hq && e.hkv == hkv && e.d == d) { e.cfg = cfg; return; }
+    g_tuned.push_back({mfma, hq, hkv, d, cfg});
+}
+
+int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
+    std::string why;
+    if (!valid_cache(a.cache, &why)) return fail(Q8K4V_EINVAL, "attention: " + why);
+    const int32_t H = a.cache->num_kv_heads;
+    const int32_t D = a.cache->head_dim;
+    if (a.n_seqs < 1) return fail(Q8K4V_EINVAL, "attention: n_seqs must be >= 1");
+    if (a.num_q_heads < 1 || a.num_q_heads % H) return fail(Q8K4V_EINVAL, "attention: num_q_heads must be a positive multiple of num_kv_heads");
+    const int32_t G = a.num_q_heads / H;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(Q8K4V_EUNSUPPORTED, "attention: group size num_q_heads/num_kv_heads must be 1, 2, 4 or 8");
+    if (a.n_draft < 1 || a.n_draft > Q8K4V_MAX_DRAFT) return fail(Q8K4V_EINVAL, "attention: n_draft must be in 1..16");
+    if (a.max_seq_len < 0) return fail(Q8K4V_EINVAL, "attention: max_seq_len must be >= 0");
+    if (a.max_pages < 1 || (int64_t)a.max_pages * Q8K4V_PAGE_SIZE < a.max_seq_len)
+        return fail(Q8K4V_EINVAL, "attention: max_pages * 16 must cover max_seq_len");
+    if (a.q_dtype != Q8K4V_F32 && a.q_dtype != Q8K4V_BF16) return fail(Q8K4V_EINVAL, "attention: q_dtype must be F32 or BF16");
+    if (!a.q || !a.out || !a.seq_lens || !a.page_table) return fail(Q8K4V_EINVAL, "attention: NULL q/out/seq_lens/page_table");
+    (void)D;
+
+    const int32_t rows = a.n_draft * G;
+    const bool dense = rows > 8;
+    if (!dense && rows != 1 && rows != 2 && rows != 4 && rows != 8)
+        return fail(Q8K4V_EUNSUPPORTED, "attention: n_draft * group must be 1, 2, 4, 8 or above 8");
+    q8k4v_config cfg;
+    if (cfg_in) cfg = *cfg_in;
+    else if (!tuned_lookup(dense, a.num_q_heads, H, D, &cfg)) cfg = default_config(dense);
+    const q8k4v_config dflt = default_config(dense);
+    if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = dflt.wgs_per_cu;
+    if (cfg.tile_pages <= 0) cfg.tile_pages = dflt.tile_pages;
+    if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = dflt.waves_per_wg;
+    if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4)
+        return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
+
+    int32_t kernel;
+    if (dense) {
+        if (cfg.variant != 0 && cfg.variant != 3) return fail(Q8K4V_EINVAL, "attention: more than 8 rows need variant 0 or 3");
+        kernel = kMfma;
+    } else if (cfg.variant == 1 || rows <= 2) {
+        if (cfg.variant != 0 && cfg.variant != 1) return fail(Q8K4V_EINVAL, "attention: 1 or 2 rows need variant 0 or 1");
+        kernel = kVector;
+    } else {
+        if (cfg.variant != 0 && cfg.variant != 2) return fail(Q8K4V_EINVAL, "attention: 4 or 8 rows need variant 0, 1 or 2");
+        kernel = kBlockMfma;
+    }
+    // tile: the block-MFMA kernel works on 4-page tiles, the dense one on 2
+    if (kernel == kBlockMfma) cfg.tile_pages = 4;
+    if (kernel == kMfma) cfg.tile_pages = 2;
+    if (cfg.tile_pages != 1 && cfg.tile_pages != 2 && cfg.tile_pages != 4)
+        return fail(Q8K4V_EINVAL, "attention: tile_pages must be 1, 2 or 4");
+
+    plan->rows = rows;
+    plan->kernel = kernel;
+    plan->mfma = dense;
+    plan->tile_pages = cfg.tile_pages;
+    plan->waves = cfg.waves_per_wg;
+    plan->rows_per_wg = (kernel == kMfma) ? (rows > 16 ? 32 : 16) : rows;
+    plan->row_chunks = (rows + plan->rows_per_wg - 1) / plan->rows_per_wg;
+    const int32_t max_np = std::max(1, (a.max_seq_len + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE);
+    const int32_t unit = cfg.tile_pages * cfg.waves_per_wg;      // pages per workgroup step
+    int32_t sp;
+    if (cfg.split_pages > 0) {
+        sp = round_up(cfg.split_pages, unit);
+    } else {
+        const int64_t target = (int64_t)cfg.wgs_per_cu * device_cu_count();
+        const int64_t per = (int64_t)a.n_seqs * H * plan->row_chunks;
+        const int64_t splits = std::max<int64_t>(1, (target + per - 1) / per);
+        sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);
+    }
+    sp = std::max(sp, unit);
+    plan->split_pages = sp;
+    plan->n_splits = (max_np + sp - 1) / sp;
+    if (plan->n_splits > kCombineMaxSplits) {   // the combine holds one weight per split in LDS
+        sp = round_up((max_np + kCombineMaxSplits - 1) / kCombineMaxSplits, unit);
+        plan->split_pages = sp;
+        plan->n_splits = (max_np + sp - 1) / sp;
+    }
+    plan->fused_combine = (plan->n_splits > 1 && cfg.fused_combine) ? 1 : 0;
+    const size_t rec = (size_t)(a.cache->head_dim + 4) * sizeof(float);
+    plan->partial_bytes = plan->n_splits > 1 ? (size_t)a.n_seqs * H * plan->n_splits * rows * rec : 0;
+    plan->partial_bytes = (plan->partial_bytes + 255) / 256 * 256;
+    plan->counter_bytes = plan->fused_combine ? (size_t)a.n_seqs * H * plan->row_chunks * sizeof(uint32_t) : 0;
+    if ((int64_t)a.n_seqs * H * plan->n_splits * plan->row_chunks + 8 > 0x7FFFFFFFLL)
+        return fail(Q8K4V_EINVAL, "attention: launch too large");
+    return Q8K4V_OK;
+}
+
+size_t plan_workspace(const Plan& p) { return p.partial_bytes + p.counter_bytes; }
+
+int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    const size_t need = plan_workspace(plan);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(Q8K4V_EWORKSPACE, "attention: workspace needs " + std::to_string(need) + " bytes");
+    const q8k4v_cache& c = *a.cache;
+    AttnParams kp;
+    kp.k_codes = c.k_codes;
+    kp.k_scales = c.k_scales;
+    kp.v_codes = c.v_codes;
+    kp.v_scales = c.v_scales;
+    kp.q = a.q;
+    kp.out = a.out;
+    kp.partials = (float*)workspace;
+    kp.counters = plan.counter_bytes ? (uint32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
+    kp.seq_lens = a.seq_lens;
+    kp.page_table = a.page_table;
+    kp.H = c.num_kv_heads;
+    kp.max_pages = a.max_pages;
+    kp.n_seqs = a.n_seqs;
+    kp.Hq = a.num_q_heads;
+    kp.G = a.num_q_heads / c.num_kv_heads;
+    kp.W = a.n_draft;
+    kp.R = plan.rows;
+    kp.split_pages = plan.split_pages;
+    kp.n_splits = plan.n_splits;
+    kp.row_chunks = plan.row_chunks;
+    kp.scale_log2 = a.softmax_scale * kLog2e;
+    kp.direct = plan.n_splits == 1;
+    kp.fused = plan.fused_combine;
+    const bool bf = a.q_dtype == Q8K4V_BF16;
+    int32_t rc;
+    switch (plan.kernel) {
+        case kVector: rc = launch_valu(kp, plan, c.head_dim, bf, stream); break;
+        case kBlockMfma: rc = launch_bmfma(kp, plan, c.head_dim, bf, stream); break;
+        default: rc = launch_mfma(kp, plan, c.head_dim, bf, stream); break;
+    }
+    if (rc != Q8K4V_OK) return rc;
+    if (!kp.direct && !kp.fused) return launch_combine(kp, c.head_dim, plan.rows_per_wg, stream);
+    return Q8K4V_OK;
+}
+
+}  // namespace q8k4v
+
+using namespace q8k4v;
+
+extern "C" {
+
+const char* q8k4v_last_error(void) { return g_last_error.c_str(); }
+
+const char* q8k4v_version(void) { return "q8k4v 1 gfx950 " Q8K4V_BUILD_ID; }
+
+int32_t kv_quant_append(const q8k4v_cache* cache, const void* k_new, const void* v_new, int32_t dtype,
+                        const int32_t* cu_new, const int32_t* start_pos, const int32_t* page_table,
+                        int32_t max_pages, int32_t n_seqs, int32_t total_new, hipStream_t stream) {
+    std::string why;
+    if (!valid_cache(cache, &why)) return fail(Q8K4V_EINVAL, "kv_quant_append: " + why);
+    if (dtype != Q8K4V_F32 && dtype != Q8K4V_BF16) return fail(Q8K4V_EINVAL, "kv_quant_append: dtype must be F32 or BF16");
+    if (n_seqs < 1) return fail(Q8K4V_EINVAL, "kv_quant_append: n_seqs must be >= 1");
+    if (total_new < 0) return fail(Q8K4V_EINVAL, "kv_quant_append: total_new must be >= 0");
+    if (max_pages < 1) return fail(Q8K4V_EINVAL, "kv_quant_append: max_pages must be >= 1");
+    if (total_new == 0) return Q8K4V_OK;
+    if (!k_new || !v_new || !cu_new || !start_pos || !page_table)
+        return fail(Q8K4V_EINVAL, "kv_quant_append: NULL input pointer");
+    AppendArgs a{cache, k_new, v_new, dtype, cu_new, start_pos, page_table, max_pages, n_seqs, total_new};
+    return launch_append(a, stream);
+}
+
+size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_seq_len, int32_t n_draft, const q8k4v_config* cfg) {
+    q8k4v_cache fake;
+    fake.num_pages = 1;
+    fake.num_kv_heads = num_kv_heads;
+    fake.head_dim = head_dim;
+    fake.page_size = Q8K4V_PAGE_SIZE;
+    fake.k_codes = (int8_t*)1;
+    fake.k_scales = (uint16_t*)1;
+    fake.v_codes = (uint8_t*)1;
+    fake.v_scales = (uint16_t*)1;
+    AttnArgs a{};
+    a.cache = &fake;
+    a.q = (const void*)1;
+    a.q_dtype = Q8K4V_BF16;
+    a.out = (float*)1;
+    a.n_seqs = n_seqs;
+    a.num_q_heads = num_q_heads;
+    a.n_draft = n_draft <= 0 ? 1 : n_draft;
+    a.seq_lens = (const int32_t*)1;
+    a.max_seq_len = max_seq_len;
+    a.page_table = (const int32_t*)1;
+    a.max_pages = std::max(1, (max_seq_len + 15) / 16);
+    a.softmax_scale = 1.0f;
+    Plan p;
+    std::string saved = g_last_error;
+    if (make_plan(a, cfg, &p) != Q8K4V_OK) { g_last_error = saved; return 0; }
+    return plan_workspace(p);
+}
+
+static int32_t attention_entry(const char* name, const q8k4v_cache* cache, const void* q, int32_t q_dtype,
+                               float* out, int32_t n_seqs, int32_t num_q_heads, int32_t n_draft,
+                               const int32_t* seq_lens, int32_t max_seq_len, const int32_t* page_table,
+                               int32_t max_pages, float softmax_scale, const q8k4v_config* cfg,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    AttnArgs a{cache, q, q_dtype, out, n_seqs, num_q_heads, n_draft, seq_lens, max_seq_len,
+               page_table, max_pages, softmax_scale};
+    Plan plan;
+    int32_t rc = make_plan(a, cfg, &plan);
+    if (rc != Q8K4V_OK) {
+        g_last_error = std::string(name) + ": " + g_last_error;
+        return rc;
+    }
+    return launch_attention(a, plan, workspace, workspace_bytes, stream);
+}
+
+int32_t attn_decode_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out, int32_t n_seqs,
+                          int32_t num_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
+                          const int32_t* page_table, int32_t max_pages, float softmax_scale,
+                          const q8k4v_config* cfg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return attention_entry("attn_decode_q8k4v", cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens,
+                           max_seq_len, page_table, max_pages, softmax_scale, cfg, workspace, workspace_bytes,
+                           stream);
+}
+
+int32_t attn_verify_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out, int32_t n_seqs,
+                          int32_t num_q_heads, int32_t n_draft, const int32_t* seq_lens, int32_t max_seq_len,
+                          const int32_t* page_table, int32_t max_pages, float softmax_scale,
+                          const q8k4v_config* cfg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n_draft < 1 || n_draft > Q8K4V_MAX_DRAFT) return fail(Q8K4V_EINVAL, "attn_verify_q8k4v: n_draft must be in 1..16");
+    if (max_seq_len < n_draft) return fail(Q8K4V_EINVAL, "attn_verify_q8k4v: max_seq_len must hold the drafts");
+    return attention_entry("attn_verify_q8k4v", cache, q, q_dtype, out, n_seqs, num_q_heads, n_draft, seq_lens,
+                           max_seq_len, page_table, max_pages, softmax_scale, cfg, workspace, workspace_bytes,
+                           stream);
+}
+
+}  // extern "C"

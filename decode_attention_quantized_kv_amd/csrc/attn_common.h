@@ -1,0 +1,253 @@
+// Pieces shared by the three attention kernels (vector, 4x4x4 block MFMA,
+// 16x16 MFMA): launch parameters, the XCD-aware work-item mapping, the merge
+// of a workgroup's waves, the split partials and the log-sum-exp combine of
+// the splits (by the last-arriving workgroup or by a separate kernel).
+#pragma once
+
+#include "q8k4v_device.h"
+
+namespace q8k4v {
+
+struct AttnParams {
+    const int8_t* __restrict__ k_codes;
+    const uint16_t* __restrict__ k_scales;
+    const uint8_t* __restrict__ v_codes;
+    const uint16_t* __restrict__ v_scales;
+    const void* __restrict__ q;
+    float* __restrict__ out;
+    float* __restrict__ partials;      // [n_seqs][H][n_splits][R][D + 4]
+    uint32_t* __restrict__ counters;   // [n_seqs][H] arrivals (fused combine)
+    const int32_t* __restrict__ seq_lens;
+    const int32_t* __restrict__ page_table;
+    int32_t H, max_pages, n_seqs, Hq, G, W, R;
+    int32_t split_pages, n_splits, row_chunks;
+    float scale_log2;                  // softmax scale * log2(e)
+    int32_t direct;                    // one split: write normalised output
+    int32_t fused;                     // last workgroup merges the splits
+};
+
+constexpr float kNegInf = -__builtin_inff();
+
+// Split partials cross XCDs (each XCD has its own L2).  They are written with
+// agent-scope atomic stores, which write through to the device-coherent level,
+// and read back with agent-scope atomic loads, so the merge needs no L2
+// writeback or invalidation.
+Q8K4V_DEV void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+Q8K4V_DEV float load_coherent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+constexpr int partial_stride() { return D + 4; }   // m, l, pad, pad, o[D]
+
+struct WorkItem {
+    int b, kh, split, rchunk, L, npages, pbeg, pend;
+};
+
+// Work items (sequence, split, kv head, row chunk) are numbered so that
+// consecutive items are the kv heads of one split; the dispatcher hands
+// workgroup i to XCD i % 8, so item = xcd * per_xcd + i / 8 keeps a split's
+// heads (which share the lines of the key-scale pool) on one XCD's L2.
+Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w) {
+    const int total = p.n_seqs * p.H * p.n_splits * p.row_chunks;
+    const int per_xcd = (total + 7) >> 3;
+    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (item >= total) return false;
+    w.rchunk = item % p.row_chunks;
+    const int it = item / p.row_chunks;
+    w.kh = it % p.H;
+    w.split = (it / p.H) % p.n_splits;
+    w.b = it / (p.H * p.n_splits);
+    w.L = p.seq_lens[w.b];
+    w.npages = (w.L + 15) >> 4;
+    w.pbeg = w.split * p.split_pages;
+    w.pend = min(w.npages, w.pbeg + p.split_pages);
+    return true;
+}
+
+Q8K4V_DEV size_t out_index(const AttnParams& p, int b, int kh, int r, int D) {
+    const int j = r / p.G, g = r % p.G;
+    return (((size_t)b * p.W + j) * p.Hq + kh * p.G + g) * D;
+}
+
+// Empty split of a single-split launch: the sequence has no tokens, its
+// output rows are zero.
+template <int D>
+Q8K4V_DEV void write_zero_rows(const AttnParams& p, const WorkItem& w, int r0, int nrows) {
+    for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) {
+        const int r = r0 + e / D;
+        if (r < p.R) p.out[out_index(p, w.b, w.kh, r, D) + e % D] = 0.0f;
+    }
+}
+
+// Log-sum-exp merge of the n_eff split partials of (b, kh) for rows
+// [r0, r0 + NR), by the threads of one workgroup: one wave per row gathers
+// the split maxima and sums in parallel, then every thread streams the
+// partial outputs of its (row, dimension) elements with independent loads.
+constexpr int kCombineMaxSplits = 1024;
+
+template <int D, int NR>
+Q8K4V_DEV void combine_splits(const AttnParams& p, int b, int kh, int r0, int n_eff) {
+    __shared__ float s_ref[NR], s_inv[NR];
+    const size_t rs = (size_t)p.R * partial_stride<D>();
+    const float* base = p.partials + ((size_t)b * p.H + kh) * p.n_splits * rs;
+    const int nt = blockDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = nt >> 6;
+    for (int rl = wave; rl < NR; rl += nw) {
+        const int r = r0 + rl;
+        float M = kNegInf;
+        if (r < p.R)
+            for (int s = lane; s < n_eff; s += 64) M = fmaxf(M, load_coherent(base + s * rs + (size_t)r * partial_stride<D>()));
+        for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float ref = (M == kNegInf) ? 0.0f : M;
+        float Ls = 0.0f;
+        if (r < p.R)
+            for (int s = lane; s < n_eff; s += 64) {
+                const float* rec = base + s * rs + (size_t)r * partial_stride<D>();
+                Ls += load_coherent(rec + 1) * exp2_fast(load_coherent(rec) - ref);
+            }
+        for (int o = 1; o < 64; o <<= 1) Ls += __shfl_xor(Ls, o);
+        if (lane == 0) {
+            s_ref[rl] = ref;
+            s_inv[rl] = (Ls > 0.0f) ? 1.0f / Ls : 0.0f;
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < NR * D; e += nt) {
+        const int rl = e / D, d = e % D;
+        const int r = r0 + rl;
+        if (r >= p.R) continue;
+        const float ref = s_ref[rl];
+        const float* rec = base + (size_t)r * partial_stride<D>();
+        float O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
+        int s = 0;
+        for (; s + 4 <= n_eff; s += 4) {
+            O0 += load_coherent(rec + (s + 0) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 0) * rs) - ref);
+            O1 += load_coherent(rec + (s + 1) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 1) * rs) - ref);
+            O2 += load_coherent(rec + (s + 2) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 2) * rs) - ref);
+            O3 += load_coherent(rec + (s + 3) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 3) * rs) - ref);
+        }
+        for (; s < n_eff; ++s) O0 += load_coherent(rec + s * rs + 4 + d) * exp2_fast(load_coherent(rec + s * rs) - ref);
+        p.out[out_index(p, b, kh, r, D) + d] = ((O0 + O1) + (O2 + O3)) * s_inv[rl];
+    }
+}
+
+// Merge the waves of a workgroup (each wave left its running max m, sum l
+// and unnormalised output o in LDS), then write the normalised output (one
+// split) or the split partial; with the fused combine the last workgroup of
+// (b, kh) to arrive merges all splits.
+template <int D, int RW, int WAVES>
+Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
+                                const float (*s_ml)[RW][2], const float* s_o /* [WAVES][RW][D] */) {
+    __syncthreads();
+    const size_t rs = (size_t)p.R * partial_stride<D>();
+    for (int e = threadIdx.x; e < RW * D; e += 64 * WAVES) {
+        const int rl = e / D, d = e % D;
+        const int r = r0 + rl;
+        if (r >= p.R) continue;
+        float M = kNegInf;
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) M = fmaxf(M, s_ml[wv][rl][0]);
+        const float ref = (M == kNegInf) ? 0.0f : M;
+        float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) {
+            const float f = exp2_fast(s_ml[wv][rl][0] - ref);
+            Ls += s_ml[wv][rl][1] * f;
+            O += s_o[(wv * RW + rl) * D + d] * f;
+        }
+        if (p.direct) {
+            p.out[out_index(p, w.b, w.kh, r, D) + d] = (Ls > 0.0f) ? O / Ls : 0.0f;
+        } else {
+            float* rec = p.partials + ((size_t)w.b * p.H + w.kh) * p.n_splits * rs + w.split * rs +
+                         (size_t)r * partial_stride<D>();
+            if (d == 0) { store_coherent(rec, M); store_coherent(rec + 1, Ls); }
+            store_coherent(rec + 4 + d, O);
+        }
+    }
+    if (p.direct || !p.fused) return;
+    // ---- fused combine: count arrivals of this (b, kh, row chunk)
+    __shared__ int s_last;
+    const int n_eff = (w.npages + p.split_pages - 1) / p.split_pages;
+    // every thread's write-through stores have completed before the barrier
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t* ctr = p.counters + ((size_t)w.b * p.H + w.kh) * p.row_chunks + w.rchunk;
+        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old + 1 == (uint32_t)n_eff);
+        if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    combine_splits<D, RW>(p, w.b, w.kh, r0, n_eff);
+}
+
+// Separate combine kernel: one 256-thread workgroup per (b, kh, row).  All
+// split records of the row are loaded at once: first the per-split (max,
+// sum) pairs, reduced to the row's reference and weights in LDS; then the
+// partial outputs as float4 columns, each thread summing a strided subset of
+// the splits, and a tree over the subsets.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
+    constexpr int NQ = D / 4;                 // float4 columns of a row
+    constexpr int SG = 256 / NQ;              // split groups
+    __shared__ float s_w[kCombineMaxSplits];
+    __shared__ float s_red[8];
+    __shared__ f32x4 s_acc[SG][NQ];
+    const int t = threadIdx.x;
+    const int r = blockIdx.x % p.R;
+    const int kh = (blockIdx.x / p.R) % p.H;
+    const int b = blockIdx.x / (p.R * p.H);
+    const int L = p.seq_lens[b];
+    const int npages = (L + 15) >> 4;
+    const int n_eff = min(p.n_splits, (npages + p.split_pages - 1) / p.split_pages);
+    const size_t rs = (size_t)p.R * partial_stride<D>();
+    const float* base = p.partials + ((size_t)b * p.H + kh) * p.n_splits * rs + (size_t)r * partial_stride<D>();
+    // phase 1: reference max and weights
+    float M = kNegInf;
+    for (int s = t; s < n_eff; s += 256) {
+        const float m = load_coherent(base + s * rs);
+        s_w[s] = m;
+        M = fmaxf(M, m);
+    }
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if ((t & 63) == 0) s_red[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float ref = (M == kNegInf) ? 0.0f : M;
+    float Ls = 0.0f;
+    for (int s = t; s < n_eff; s += 256) {
+        const float wgt = exp2_fast(s_w[s] - ref);
+        s_w[s] = wgt;
+        Ls += load_coherent(base + s * rs + 1) * wgt;
+    }
+    for (int o = 1; o < 64; o <<= 1) Ls += __shfl_xor(Ls, o);
+    __syncthreads();
+    if ((t & 63) == 0) s_red[4 + (t >> 6)] = Ls;
+    __syncthreads();
+    const float Lt = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+    // phase 2: weighted sum of the partial outputs
+    const int qc = t % NQ, sg = t / NQ;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4* col = (const f32x4*)(base + 4) + qc;
+#pragma unroll 8
+    for (int s = sg; s < n_eff; s += SG) {
+        const f32x4 v = *(col + s * (rs / 4));
+        acc += v * s_w[s];
+    }
+    s_acc[sg][qc] = acc;
+    __syncthreads();
+    if (t < NQ) {
+        f32x4 sum = s_acc[0][t];
+#pragma unroll
+        for (int g = 1; g < SG; ++g) sum += s_acc[g][t];
+        const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
+        f32x4* dst = (f32x4*)(p.out + out_index(p, b, kh, r, D)) + t;
+        *dst = sum * inv;
+    }
+}
+
+}  // namespace q8k4v

@@ -1,0 +1,253 @@
+/*
+ * q8k4v.h -- C ABI of the int8-key / int4-value quantized-KV decode and
+ * speculative-verify attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The operations
+ * --------------
+ * The cache codec and the decode unit follow the engine described in the blog
+ * post blog.123qwe.co.kr/?p=3927, section 5 (speculative decoding, quantized
+ * KV, prefix sharing): the decode attention unit reads a "k8v4" cache whose
+ * keys are 8-bit and whose values are 4-bit in groups of 32 along the head
+ * dimension, each with an fp16 scale.  The same page (section 5, first table)
+ * states that verifying several draft tokens should cost what one decode step
+ * costs because decode is bound by memory bandwidth; attn_verify_q8k4v is that
+ * pass.  Section 3 of the same page describes the first-load tuner (a 60 s
+ * wall-clock budget, a weighted service cost normalised by the time of the
+ * defaults, timing passes whose working set exceeds the last-level cache,
+ * output-preserving candidates only); tune_select is that tuner for the two
+ * attention units.  Section 4 gives the precision policy (alpha = 8) used as
+ * the tuner's admission gate.
+ *
+ * Codec (symmetric absmax, round half to even, IEEE fp32 divisions):
+ *   keys   : per (token, kv head)          s = fp16(max|x| / 127), code = clamp(rint(x / s), +-127)
+ *   values : per (token, kv head, 32 dims) s = fp16(max|x| / 7),   code = clamp(rint(x / s), +-7)
+ *   fp16 overflow of s saturates to 65504; s == 0 gives zero codes.
+ *
+ * Paged layout (page = 16 tokens; P pages, H kv heads, head dim D in {64,128}):
+ *   k_codes  int8  [P][H][16][D]     two's complement, one row per token
+ *   k_scales fp16  [P][H][16]        (uint16 bit patterns)
+ *   v_codes  uint8 [P][H][D][8]      row d holds dimension d of the 16 tokens:
+ *                                    byte j = code(slot 2j) & 0xF | (code(slot 2j+1) & 0xF) << 4
+ *   v_scales fp16  [P][H][16][D/32]
+ *   Token p of sequence b lives at page page_table[b * max_pages + p / 16], slot p % 16.
+ *
+ * Conventions
+ * -----------
+ * Pointers documented "device" are device memory of the current HIP device;
+ * "host" pointers are read during the call only.  The caller owns every
+ * buffer and the stream.  Hot-path calls (append, decode, verify) only
+ * enqueue work on `stream`: they never allocate, never synchronise and keep
+ * no device state between calls.  Device-resident values (lengths, page ids,
+ * positions) are not validated: an out-of-range value is undefined
+ * behaviour.  Every function returns Q8K4V_OK or a negative error code; the
+ * message of the last error on the calling thread is q8k4v_last_error().
+ */
+#ifndef Q8K4V_H
+#define Q8K4V_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8K4V_OK            0
+#define Q8K4V_EINVAL       -1   /* bad argument (null pointer, shape, range)     */
+#define Q8K4V_EUNSUPPORTED -2   /* valid but not built (e.g. head_dim 96)         */
+#define Q8K4V_EWORKSPACE   -3   /* workspace missing or smaller than required     */
+#define Q8K4V_EHIP         -4   /* a HIP runtime call failed                      */
+#define Q8K4V_ENOMEM       -5   /* the tuner's memory admission refused the work  */
+
+#define Q8K4V_F32  0            /* float32 values                                 */
+#define Q8K4V_BF16 1            /* bfloat16 bit patterns (uint16)                 */
+
+#define Q8K4V_PAGE_SIZE 16
+#define Q8K4V_MAX_DRAFT 16
+
+/* The paged cache: four device pools in the layout above. */
+typedef struct q8k4v_cache {
+    int32_t   num_pages;     /* P: physical pages in each pool                   */
+    int32_t   num_kv_heads;  /* H                                                */
+    int32_t   head_dim;      /* D: 64 or 128                                     */
+    int32_t   page_size;     /* must be 16                                       */
+    int8_t   *k_codes;       /* device [P][H][16][D]                             */
+    uint16_t *k_scales;      /* device [P][H][16]                                */
+    uint8_t  *v_codes;       /* device [P][H][D][8]                              */
+    uint16_t *v_scales;      /* device [P][H][16][D/32]                          */
+} q8k4v_cache;
+
+/* Launch configuration of the attention kernels (what the tuner chooses).
+ * Any field left 0 takes the library default. */
+typedef struct q8k4v_config {
+    int32_t wgs_per_cu;      /* split-K: target workgroups per compute unit; the split
+                                length follows from it and the launch shape           */
+    int32_t split_pages;     /* if > 0: pages per workgroup split (overrides wgs_per_cu) */
+    int32_t tile_pages;      /* pages staged in LDS per wave per step: 1, 2 or 4       */
+    int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup                          */
+    int32_t fused_combine;   /* 1: the last workgroup of a (sequence, kv head) merges
+                                the splits (needs a zeroed workspace counter area);
+                                0: a separate combine kernel                           */
+    int32_t qualified;       /* out of tune_select: 1 measured and admitted, 0 default */
+    int32_t variant;         /* 0 auto; 1 vector ALUs only; 2 4x4x4 block MFMA (4 or 8
+                                query rows per kv head); 3 16x16 MFMA (more than 8 rows) */
+    int32_t reserved;
+} q8k4v_config;
+
+/* Last error message of the calling thread ("" if none). */
+const char *q8k4v_last_error(void);
+
+/* Library build identity, e.g. "q8k4v 1 gfx950 <hash>". */
+const char *q8k4v_version(void);
+
+/*
+ * kv_quant_append -- quantize new tokens and write them into the paged cache.
+ *
+ * Implements the codec above (blog.123qwe.co.kr/?p=3927, section 5: 8-bit
+ * keys, 4-bit values in groups of 32 with fp16 scales).  New tokens of
+ * sequence b are rows cu_new[b] .. cu_new[b+1]-1 of k_new / v_new and go to
+ * logical positions start_pos[b], start_pos[b]+1, ... of that sequence.
+ *
+ *   cache      host pointer to the cache descriptor (device pools)
+ *   k_new      device [total_new][H][D], dtype `dtype` (Q8K4V_F32 or Q8K4V_BF16)
+ *   v_new      device [total_new][H][D], same dtype
+ *   cu_new     device int32 [n_seqs + 1], cu_new[0] = 0, nondecreasing, cu_new[n_seqs] = total_new
+ *   start_pos  device int32 [n_seqs]
+ *   page_table device int32 [n_seqs][max_pages]; every written slot's page must be
+ *              owned by that sequence (pages shared by several sequences are read-only)
+ *   total_new  host: number of new tokens (sizes the grid); 0 is a no-op
+ * Codes and scales are bit-exact with the rule above (IEEE division,
+ * round-half-even, no flush of fp16 subnormal scales).
+ * Errors: EINVAL on null pointers, D not in {64,128}, page_size != 16,
+ * n_seqs < 1, total_new < 0, bad dtype; EHIP if the launch fails.
+ */
+int32_t kv_quant_append(const q8k4v_cache *cache, const void *k_new, const void *v_new,
+                        int32_t dtype, const int32_t *cu_new, const int32_t *start_pos,
+                        const int32_t *page_table, int32_t max_pages, int32_t n_seqs,
+                        int32_t total_new, hipStream_t stream);
+
+/*
+ * Workspace (bytes) that attn_decode_q8k4v / attn_verify_q8k4v need for the
+ * given launch shape and configuration (cfg may be NULL for the defaults);
+ * n_draft = 0 for decode.  Returns 0 on invalid shapes.  The workspace holds
+ * the split-K partials and, with fused_combine, a counter area that must be
+ * zero when first used; the library leaves the counters at zero after each
+ * completed call, so zero the workspace once after allocating it.
+ */
+size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_seq_len, int32_t n_draft,
+                             const q8k4v_config *cfg);
+
+/*
+ * attn_decode_q8k4v -- one query token per sequence attends its whole cache.
+ *
+ * Exact softmax attention over the dequantized cache (the decode unit of
+ * blog.123qwe.co.kr/?p=3927, section 5), computed split-K: workgroups
+ * each take a range of pages of one (sequence, kv head), stage K/V pages in
+ * LDS, dequantize in registers, keep an online softmax, and the splits are
+ * merged by log-sum-exp.  Query head h reads kv head h / (num_q_heads / H).
+ *
+ *   q            device [n_seqs][num_q_heads][D], dtype q_dtype (F32 or BF16)
+ *   out          device float32 [n_seqs][num_q_heads][D]
+ *   seq_lens     device int32 [n_seqs]: cached tokens attended (0 gives zeros)
+ *   max_seq_len  host: an upper bound of seq_lens (sizes the grid)
+ *   page_table   device int32 [n_seqs][max_pages]
+ *   softmax_scale  multiplies q.k (e.g. 1/sqrt(D))
+ *   cfg          host, NULL = tuned table or defaults
+ *   workspace    device, at least q8k4v_workspace_bytes(...) bytes
+ * Supported: D in {64,128}, num_q_heads / H in {1,2,4,8}.
+ * Errors: EINVAL (shapes, null pointers), EUNSUPPORTED (group size),
+ * EWORKSPACE (workspace too small), EHIP.
+ */
+int32_t attn_decode_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dtype,
+                          float *out, int32_t n_seqs, int32_t num_q_heads,
+                          const int32_t *seq_lens, int32_t max_seq_len,
+                          const int32_t *page_table, int32_t max_pages, float softmax_scale,
+                          const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * attn_verify_q8k4v -- n_draft draft queries per sequence, causal among the
+ * drafts (blog.123qwe.co.kr/?p=3927, section 5: checking several drafted
+ * tokens in the pass that one decode step costs).
+ *
+ * The drafts' keys/values must already be appended: seq_lens[b] counts them,
+ * and draft j (0-based) of sequence b attends positions 0 .. seq_lens[b] -
+ * n_draft + j.  Rows (draft, q head) of one kv head form a
+ * (n_draft * group) x D query block; when that block has more than 8 rows it
+ * is a dense contraction and runs on MFMA (fp16 operands: bf16/fp32 queries
+ * pre-scaled by a power of two, exact int8/int4 codes, fp16 probabilities
+ * folded with the value scales, fp32 accumulation); up to 8 rows it runs on
+ * the vector path of attn_decode_q8k4v.
+ *
+ *   q, out   [n_seqs][n_draft][num_q_heads][D] (q dtype q_dtype, out float32)
+ *   n_draft  1 .. Q8K4V_MAX_DRAFT; every seq_lens[b] >= n_draft
+ * Other arguments and errors as attn_decode_q8k4v.
+ */
+int32_t attn_verify_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dtype,
+                          float *out, int32_t n_seqs, int32_t num_q_heads, int32_t n_draft,
+                          const int32_t *seq_lens, int32_t max_seq_len,
+                          const int32_t *page_table, int32_t max_pages, float softmax_scale,
+                          const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * tune_select -- on-device search of the attention launch configuration
+ * (blog.123qwe.co.kr/?p=3927, section 3: first-load tuner).
+ *
+ * For each unit (decode, verify) it measures candidate configurations on
+ * four shapes -- decode and verify at ctx_small and ctx_large -- and keeps,
+ * per unit, the admitted candidate with the least service cost
+ *     cost(c) = sum over the unit's shapes p of median_time(c, p) / median_time(default, p)
+ * (term weights 1, one launch per layer-step).  Every step -- allocation,
+ * input synthesis, the defaults' measurement, the candidates, the gate --
+ * runs inside the wall-clock budget (at most 60 s); a candidate not measured
+ * before the deadline is "unknown" and never admitted.  Timing rotates over
+ * distinct cache copies whose total size exceeds 4 x 256 MiB (the MI355X
+ * last-level cache), so no pass is served from a warm cache.  Admission
+ * (section 4 of the same page, alpha = 8): on every checked output the
+ * candidate's deviation from the default configuration's output must not
+ * exceed alpha times the storage-resolution noise, i.e. the change of the
+ * default output when every stored code is moved by one step; and, when the
+ * caller supplies reference outputs, the deviation from them must not
+ * exceed ref_tol.
+ *
+ *   req         host, see q8k4v_tune_request
+ *   out_table   host [2]: [0] decode, [1] verify; `qualified` = 1 if a
+ *               measured candidate was admitted, else the defaults with 0
+ *   report_json host buffer for a JSON report (may be NULL), NUL-terminated
+ * Returns Q8K4V_OK even when nothing could be searched (defaults,
+ * unqualified); ENOMEM if memory admission refuses even the defaults;
+ * EINVAL on bad shapes; EHIP.
+ */
+typedef struct q8k4v_tune_request {
+    int32_t num_q_heads, num_kv_heads, head_dim, n_draft;
+    int32_t ctx_small, ctx_large;      /* e.g. 4096 and 65536 */
+    int64_t budget_ms;                 /* wall clock, clamped to 60000 */
+    size_t  mem_cap_bytes;             /* 0: free device memory at the call */
+    uint64_t seed;                     /* synthetic cache contents */
+    int32_t install;                   /* 1: winners become the defaults used when cfg == NULL
+                                          for this (heads, head_dim) shape */
+    int32_t max_candidates;            /* 0: no limit */
+    /* optional gate against caller references on caller inputs (may be NULL):
+       ref_cache + ref_q/ref_out for decode at ref_len (one sequence) */
+    const q8k4v_cache *ref_cache;
+    const void *ref_q;                 /* device, bf16 [num_q_heads][D] (decode)            */
+    const void *ref_q_verify;          /* device, bf16 [n_draft][num_q_heads][D] (verify)    */
+    const int32_t *ref_page_table;     /* device int32 [ref_max_pages]                      */
+    int32_t ref_len, ref_max_pages;
+    const float *ref_out;              /* host float32 [num_q_heads][D]                     */
+    const float *ref_out_verify;       /* host float32 [n_draft][num_q_heads][D]            */
+    float ref_tol;                     /* absolute tolerance against the references         */
+    float softmax_scale;               /* 0: 1/sqrt(D)                                      */
+} q8k4v_tune_request;
+
+int32_t tune_select(const q8k4v_tune_request *req, q8k4v_config *out_table,
+                    char *report_json, size_t report_cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8K4V_H */

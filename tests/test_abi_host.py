@@ -1,0 +1,97 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function the public header declares, and its argument validation
+rejects bad calls before any device work."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_attention_quantized_kv_amd as q8
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "q8k4v.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q8.LIB_PATH):
+        pytest.skip("library not built")
+    return q8.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for n in ("kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", q8.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in _declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_version_string(lib):
+    assert q8.version().startswith("q8k4v 1 gfx950")
+
+
+def _desc(head_dim=128, page_size=16):
+    return q8.CacheDesc(4, 2, head_dim, page_size, 1, 1, 1, 1)
+
+
+def test_append_rejects_bad_arguments(lib):
+    d = _desc(head_dim=96)
+    rc = lib.kv_quant_append(C.byref(d), 1, 1, 1, 1, 1, 1, 1, 1, 1, None)
+    assert rc == -1 and b"head_dim" in lib.q8k4v_last_error()
+    d = _desc(page_size=32)
+    assert lib.kv_quant_append(C.byref(d), 1, 1, 1, 1, 1, 1, 1, 1, 1, None) == -1
+    d = _desc()
+    assert lib.kv_quant_append(C.byref(d), 1, 1, 7, 1, 1, 1, 1, 1, 1, None) == -1     # dtype
+    assert lib.kv_quant_append(C.byref(d), None, 1, 1, 1, 1, 1, 1, 1, 1, None) == -1  # NULL k
+    assert lib.kv_quant_append(C.byref(d), 1, 1, 1, 1, 1, 1, 1, 1, 0, None) == 0      # nothing to do
+    assert lib.kv_quant_append(None, 1, 1, 1, 1, 1, 1, 1, 1, 1, None) == -1
+
+
+def test_attention_rejects_bad_arguments(lib):
+    d = _desc()
+    args = dict(q=1, qd=1, out=1, n=1, hq=8, lens=1, msl=64, pt=1, mp=4)
+
+    def dec(**kw):
+        a = {**args, **kw}
+        return lib.attn_decode_q8k4v(C.byref(d), a["q"], a["qd"], a["out"], a["n"], a["hq"], a["lens"], a["msl"],
+                                     a["pt"], a["mp"], 0.1, None, None, 0, None)
+    assert dec(hq=7) == -1                      # not a multiple of the kv heads
+    assert dec(hq=6) == -2                      # group 3 unsupported
+    assert dec(hq=32) == -2                     # group 16 unsupported
+    assert dec(qd=5) == -1
+    assert dec(mp=2) == -1                      # page table too short for max_seq_len
+    assert dec(n=0) == -1
+    assert dec(q=None) == -1
+    assert lib.attn_verify_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 17, 1, 64, 1, 4, 0.1, None, None, 0, None) == -1
+    assert lib.attn_verify_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 3, 1, 2, 1, 4, 0.1, None, None, 0, None) == -1
+    # workspace too small (needs split partials at this length)
+    d2 = q8.CacheDesc(4096, 8, 128, 16, 1, 1, 1, 1)
+    rc = lib.attn_decode_q8k4v(C.byref(d2), 1, 1, 1, 1, 32, 1, 65536, 1, 4096, 0.1, None, None, 0, None)
+    assert rc == -3 and b"workspace" in lib.q8k4v_last_error()
+
+
+def test_workspace_size_follows_the_plan(lib):
+    small = q8.workspace_bytes(1, 32, 8, 128, 64)
+    big = q8.workspace_bytes(1, 32, 8, 128, 65536)
+    assert big > 0 and big >= small
+    cfg = q8.make_config(split_pages=4096)
+    assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, cfg) == 0     # one split: direct write
+    assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(waves_per_wg=3)) == 0  # invalid config
+    assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(variant=2)) == 0  # 1 row: no block MFMA
