@@ -74,6 +74,11 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library not built: {path} is missing "
                            "(run python -m decode_attention_quantized_kv_amd.build)")
+    # torch first: its bundled HIP runtime then satisfies the library's
+    # libamdhip64.so.7 dependency, so the process holds one HIP runtime (the
+    # other order loads the system runtime as well and the two do not share
+    # devices or memory)
+    import torch  # noqa: F401
     lib = C.CDLL(path)
     i32, vp, sz = C.c_int32, C.c_void_p, C.c_size_t
     lib.q8k4v_last_error.restype = C.c_char_p

@@ -115,9 +115,9 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     (void)D;
 
     const int32_t rows = a.n_draft * G;
-    const bool dense = rows > 8;
-    if (!dense && rows != 1 && rows != 2 && rows != 4 && rows != 8)
-        return fail(Q8K4V_EUNSUPPORTED, "attention: n_draft * group must be 1, 2, 4, 8 or above 8");
+    // 1, 2, 4 or 8 rows per kv head fit the vector and block-MFMA kernels;
+    // any other row count goes to the dense-MFMA kernel (masked to 16/32 rows)
+    const bool dense = rows != 1 && rows != 2 && rows != 4 && rows != 8;
     q8k4v_config cfg;
     if (cfg_in) cfg = *cfg_in;
     else if (!tuned_lookup(dense, a.num_q_heads, H, D, &cfg)) cfg = default_config(dense);
@@ -130,7 +130,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
 
     int32_t kernel;
     if (dense) {
-        if (cfg.variant != 0 && cfg.variant != 3) return fail(Q8K4V_EINVAL, "attention: more than 8 rows need variant 0 or 3");
+        if (cfg.variant != 0 && cfg.variant != 3) return fail(Q8K4V_EINVAL, "attention: row counts other than 1, 2, 4, 8 need variant 0 or 3");
         kernel = kMfma;
     } else if (cfg.variant == 1 || rows <= 2) {
         if (cfg.variant != 0 && cfg.variant != 1) return fail(Q8K4V_EINVAL, "attention: 1 or 2 rows need variant 0 or 1");

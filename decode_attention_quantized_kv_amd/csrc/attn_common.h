@@ -134,15 +134,48 @@ Q8K4V_DEV void combine_splits(const AttnParams& p, int b, int kh, int r0, int n_
     }
 }
 
+// Write one merged (row, dimension) element of a workgroup: the normalised
+// output when there is a single split, else the split partial.
+template <int D>
+Q8K4V_DEV void emit_element(const AttnParams& p, const WorkItem& w, int r, int d, float M, float Ls, float O) {
+    if (p.direct) {
+        p.out[out_index(p, w.b, w.kh, r, D) + d] = (Ls > 0.0f) ? O / Ls : 0.0f;
+    } else {
+        const size_t rs = (size_t)p.R * partial_stride<D>();
+        float* rec = p.partials + ((size_t)w.b * p.H + w.kh) * p.n_splits * rs + w.split * rs +
+                     (size_t)r * partial_stride<D>();
+        if (d == 0) { store_coherent(rec, M); store_coherent(rec + 1, Ls); }
+        store_coherent(rec + 4 + d, O);
+    }
+}
+
+// With the fused combine, the last workgroup of (b, kh, row chunk) to finish
+// merges all splits.  Called by every thread after its emit_element calls.
+template <int D, int RW>
+Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0) {
+    if (p.direct || !p.fused) return;
+    __shared__ int s_last;
+    const int n_eff = (w.npages + p.split_pages - 1) / p.split_pages;
+    // every thread's write-through stores have completed before the barrier
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t* ctr = p.counters + ((size_t)w.b * p.H + w.kh) * p.row_chunks + w.rchunk;
+        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old + 1 == (uint32_t)n_eff);
+        if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    combine_splits<D, RW>(p, w.b, w.kh, r0, n_eff);
+}
+
 // Merge the waves of a workgroup (each wave left its running max m, sum l
-// and unnormalised output o in LDS), then write the normalised output (one
-// split) or the split partial; with the fused combine the last workgroup of
-// (b, kh) to arrive merges all splits.
+// and unnormalised output o in LDS), then emit the rows.
 template <int D, int RW, int WAVES>
 Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
                                 const float (*s_ml)[RW][2], const float* s_o /* [WAVES][RW][D] */) {
     __syncthreads();
-    const size_t rs = (size_t)p.R * partial_stride<D>();
     for (int e = threadIdx.x; e < RW * D; e += 64 * WAVES) {
         const int rl = e / D, d = e % D;
         const int r = r0 + rl;
@@ -158,31 +191,9 @@ Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
             Ls += s_ml[wv][rl][1] * f;
             O += s_o[(wv * RW + rl) * D + d] * f;
         }
-        if (p.direct) {
-            p.out[out_index(p, w.b, w.kh, r, D) + d] = (Ls > 0.0f) ? O / Ls : 0.0f;
-        } else {
-            float* rec = p.partials + ((size_t)w.b * p.H + w.kh) * p.n_splits * rs + w.split * rs +
-                         (size_t)r * partial_stride<D>();
-            if (d == 0) { store_coherent(rec, M); store_coherent(rec + 1, Ls); }
-            store_coherent(rec + 4 + d, O);
-        }
+        emit_element<D>(p, w, r, d, M, Ls, O);
     }
-    if (p.direct || !p.fused) return;
-    // ---- fused combine: count arrivals of this (b, kh, row chunk)
-    __shared__ int s_last;
-    const int n_eff = (w.npages + p.split_pages - 1) / p.split_pages;
-    // every thread's write-through stores have completed before the barrier
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t* ctr = p.counters + ((size_t)w.b * p.H + w.kh) * p.row_chunks + w.rchunk;
-        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old + 1 == (uint32_t)n_eff);
-        if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    combine_splits<D, RW>(p, w.b, w.kh, r0, n_eff);
+    fused_tail<D, RW>(p, w, r0);
 }
 
 // Separate combine kernel: one 256-thread workgroup per (b, kh, row).  All

@@ -90,8 +90,9 @@ typedef struct q8k4v_config {
                                 the splits (needs a zeroed workspace counter area);
                                 0: a separate combine kernel                           */
     int32_t qualified;       /* out of tune_select: 1 measured and admitted, 0 default */
-    int32_t variant;         /* 0 auto; 1 vector ALUs only; 2 4x4x4 block MFMA (4 or 8
-                                query rows per kv head); 3 16x16 MFMA (more than 8 rows) */
+    int32_t variant;         /* 0 auto; 1 vector ALUs only (1 or 2 query rows per kv
+                                head); 2 4x4x4 block MFMA (4 or 8 rows); 3 16x16 MFMA
+                                (any other row count, masked to 16 or 32 rows)       */
     int32_t reserved;
 } q8k4v_config;
 
@@ -175,11 +176,13 @@ int32_t attn_decode_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
  * The drafts' keys/values must already be appended: seq_lens[b] counts them,
  * and draft j (0-based) of sequence b attends positions 0 .. seq_lens[b] -
  * n_draft + j.  Rows (draft, q head) of one kv head form a
- * (n_draft * group) x D query block; when that block has more than 8 rows it
- * is a dense contraction and runs on MFMA (fp16 operands: bf16/fp32 queries
- * pre-scaled by a power of two, exact int8/int4 codes, fp16 probabilities
- * folded with the value scales, fp32 accumulation); up to 8 rows it runs on
- * the vector path of attn_decode_q8k4v.
+ * (n_draft * group) x D query block.  With 1, 2, 4 or 8 rows it runs on the
+ * kernels of attn_decode_q8k4v; any other row count is a dense contraction
+ * on 16x16 MFMA tiles: q.K on int8 MFMA (raw key codes against the query as a
+ * 15-bit fixed-point number split into two int8 halves, int32 accumulation),
+ * P.V on fp16 MFMA (exact value codes against each probability times the
+ * token's value scale for that 32-dim group, rounded to fp16; fp32
+ * accumulation).
  *
  *   q, out   [n_seqs][n_draft][num_q_heads][D] (q dtype q_dtype, out float32)
  *   n_draft  1 .. Q8K4V_MAX_DRAFT; every seq_lens[b] >= n_draft
