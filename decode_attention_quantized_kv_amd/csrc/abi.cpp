@@ -26,9 +26,8 @@ int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipS
 namespace {
 thread_local std::string g_last_error;
 
-struct TunedEntry {
-    bool mfma;
-    int32_t hq, hkv, d;
+struct TunedEntry {          // keyed by device and shape; n_draft 1 is the decode unit
+    int32_t device, n_draft, hq, hkv, d;
     q8k4v_config cfg;
 };
 std::mutex g_tuned_mu;
@@ -70,12 +69,12 @@ int32_t device_cu_count() {
     return cached[dev];
 }
 
-q8k4v_config default_config(bool mfma) {
+q8k4v_config default_config(bool verify) {
     q8k4v_config c;
     std::memset(&c, 0, sizeof(c));
     c.wgs_per_cu = 5;
     c.split_pages = 0;
-    c.tile_pages = mfma ? 2 : 4;
+    c.tile_pages = verify ? 2 : 4;
     c.waves_per_wg = 2;
     c.fused_combine = 0;
     c.qualified = 0;
@@ -83,18 +82,31 @@ q8k4v_config default_config(bool mfma) {
     return c;
 }
 
-bool tuned_lookup(bool mfma, int32_t hq, int32_t hkv, int32_t d, q8k4v_config* cfg) {
+static int current_device() {
+    int dev = 0;
+    return hipGetDevice(&dev) == hipSuccess ? dev : 0;
+}
+
+bool tuned_lookup(int32_t n_draft, int32_t hq, int32_t hkv, int32_t d, q8k4v_config* cfg) {
+    const int dev = current_device();
     std::lock_guard<std::mutex> lk(g_tuned_mu);
     for (const auto& e : g_tuned)
-        if (e.mfma == mfma && e.hq == hq && e.hkv == hkv && e.d == d) { *cfg = e.cfg; return true; }
+        if (e.device == dev && e.n_draft == n_draft && e.hq == hq && e.hkv == hkv && e.d == d) {
+            *cfg = e.cfg;
+            return true;
+        }
     return false;
 }
 
-void tuned_install(bool mfma, int32_t hq, int32_t hkv, int32_t d, const q8k4v_config& cfg) {
+void tuned_install(int32_t n_draft, int32_t hq, int32_t hkv, int32_t d, const q8k4v_config& cfg) {
+    const int dev = current_device();
     std::lock_guard<std::mutex> lk(g_tuned_mu);
     for (auto& e : g_tuned)
-        if (e.mfma == mfma && e.hq == hq && e.hkv == hkv && e.d == d) { e.cfg = cfg; return; }
-    g_tuned.push_back({mfma, hq, hkv, d, cfg});
+        if (e.device == dev && e.n_draft == n_draft && e.hq == hq && e.hkv == hkv && e.d == d) {
+            e.cfg = cfg;
+            return;
+        }
+    g_tuned.push_back({dev, n_draft, hq, hkv, d, cfg});
 }
 
 int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
@@ -120,8 +132,8 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     const bool dense = rows != 1 && rows != 2 && rows != 4 && rows != 8;
     q8k4v_config cfg;
     if (cfg_in) cfg = *cfg_in;
-    else if (!tuned_lookup(dense, a.num_q_heads, H, D, &cfg)) cfg = default_config(dense);
-    const q8k4v_config dflt = default_config(dense);
+    else if (!tuned_lookup(a.n_draft, a.num_q_heads, H, D, &cfg)) cfg = default_config(a.n_draft > 1);
+    const q8k4v_config dflt = default_config(a.n_draft > 1);
     if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = dflt.wgs_per_cu;
     if (cfg.tile_pages <= 0) cfg.tile_pages = dflt.tile_pages;
     if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = dflt.waves_per_wg;

@@ -61,9 +61,9 @@ struct Plan {
     size_t counter_bytes;  // fused-combine counters
 };
 
-// Default configuration (wgs_per_cu etc.) for a unit; used when cfg is NULL
-// and no tuned entry matches.
-q8k4v_config default_config(bool mfma);
+// Default configuration (wgs_per_cu etc.) of the decode (verify = false) or
+// verify unit; used when cfg is NULL and no tuned entry matches.
+q8k4v_config default_config(bool verify);
 
 // Resolve config + shape into a plan; returns Q8K4V_OK or an error.
 int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg, Plan* plan);
@@ -72,11 +72,11 @@ size_t plan_workspace(const Plan& p);
 int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
-// Tuned table lookup (installed by tune_select); returns true and fills cfg
-// if an entry matches.
-bool tuned_lookup(bool mfma, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+// Tuned table (installed by tune_select), per current device and shape;
+// n_draft 1 is the decode unit.  lookup returns true and fills cfg on a match.
+bool tuned_lookup(int32_t n_draft, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                   q8k4v_config* cfg);
-void tuned_install(bool mfma, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+void tuned_install(int32_t n_draft, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                    const q8k4v_config& cfg);
 
 int32_t device_cu_count();

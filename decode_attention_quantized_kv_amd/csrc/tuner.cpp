@@ -1,15 +1,671 @@
-// On-device tuner (placeholder: returns the defaults, unqualified).
-#include <cstring>
+// On-device tuner of the attention launch configuration (the first-load
+// tuner of blog.123qwe.co.kr/?p=3927, section 3, with the admission rule of
+// section 4).  Contract: tune_select in include/q8k4v.h.
+//
+// Everything below runs inside one wall-clock budget (<= 60 s): memory
+// admission, synthesis of the timing caches on the device, the defaults'
+// measurements and outputs, the storage-resolution noise, the candidates and
+// their gate.  Per unit (decode: one query row block per kv head; verify:
+// n_draft drafts) the service cost of a configuration c is
+//     cost(c) = sum over the unit's two shapes p of median(c, p) / median(default, p)
+// with shapes at ctx_small and ctx_large, term weights 1, one launch per
+// layer-step.  Medians are over single launches bracketed by HIP events on
+// the tuner's own stream; launches rotate over distinct cache copies (and,
+// for the small context, over disjoint page sets) whose total exceeds four
+// times the 256 MiB last-level cache, so every launch streams from HBM.
+//
+// Order: the default, then the structural variants (which kernel), then a
+// refinement of the launch shape (waves per workgroup, workgroups per CU,
+// fused combine) around the best structural choice.  A candidate that is not
+// fully measured and checked before the deadline is "unknown" and is never
+// admitted.  Admission: on each of the unit's two shapes, the candidate's
+// output may differ from the default configuration's output by at most
+// alpha = 8 times the storage-resolution noise -- the change of the default
+// output when every stored code moves by one quantisation step -- and, when
+// the caller passes reference outputs, by at most ref_tol from them.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
 #include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
 #include "q8k4v_internal.h"
+
+namespace q8k4v {
+namespace {
+
+using Clock = std::chrono::steady_clock;
+
+constexpr double kAlpha = 8.0;
+constexpr size_t kLlcBytes = size_t(256) << 20;
+constexpr int kMaxBudgetMs = 60000;
+
+// ---- device-side synthesis (counter-based hash, no state) -----------------
+
+__device__ __forceinline__ uint32_t mix32(uint64_t x) {
+    x ^= x >> 33;
+    x *= 0xff51afd7ed558ccdULL;
+    x ^= x >> 33;
+    x *= 0xc4ceb9fe1a85ec53ULL;
+    x ^= x >> 33;
+    return (uint32_t)x;
+}
+
+__device__ __forceinline__ float unit_float(uint32_t h) { return (float)(h >> 8) * (1.0f / 16777216.0f); }
+
+// Random cache contents: key codes in -127..127, value codes in -7..7 (two
+// per byte), key scales 0.01..0.03, value scales 0.2..0.6 (the magnitudes of
+// N(0,1) data quantised per row / per 32-dim group).
+__global__ void fill_cache_kernel(int8_t* kc, uint16_t* ks, uint8_t* vc, uint16_t* vs, size_t nk, size_t nks,
+                                  size_t nv, size_t nvs, uint64_t seed) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (size_t i = i0; i < nk; i += stride) kc[i] = (int8_t)((int)(mix32(seed ^ (i * 4 + 0)) % 255u) - 127);
+    for (size_t i = i0; i < nv; i += stride) {
+        const uint32_t h = mix32(seed ^ (i * 4 + 1));
+        const int lo = (int)(h % 15u) - 7, hi = (int)((h >> 16) % 15u) - 7;
+        vc[i] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+    }
+    for (size_t i = i0; i < nks; i += stride)
+        ks[i] = __builtin_bit_cast(uint16_t, (_Float16)(0.01f + 0.02f * unit_float(mix32(seed ^ (i * 4 + 2)))));
+    for (size_t i = i0; i < nvs; i += stride)
+        vs[i] = __builtin_bit_cast(uint16_t, (_Float16)(0.2f + 0.4f * unit_float(mix32(seed ^ (i * 4 + 3)))));
+}
+
+// dst = src with every code moved one step up or down (seeded sign, kept in
+// range); scales copied unchanged.
+__global__ void perturb_cache_kernel(const int8_t* kc, const uint16_t* ks, const uint8_t* vc, const uint16_t* vs,
+                                     int8_t* dkc, uint16_t* dks, uint8_t* dvc, uint16_t* dvs, size_t nk, size_t nks,
+                                     size_t nv, size_t nvs, uint64_t seed) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (size_t i = i0; i < nk; i += stride) {
+        int c = kc[i] + ((mix32(seed ^ (i * 2)) & 1u) ? 1 : -1);
+        if (c > 127) c = 126;
+        if (c < -127) c = -126;
+        dkc[i] = (int8_t)c;
+    }
+    for (size_t i = i0; i < nv; i += stride) {
+        const uint32_t h = mix32(seed ^ (i * 2 + 1));
+        const uint8_t b = vc[i];
+        int lo = (int)(b & 0xF), hi = (int)(b >> 4);
+        lo = lo >= 8 ? lo - 16 : lo;
+        hi = hi >= 8 ? hi - 16 : hi;
+        lo += (h & 1u) ? 1 : -1;
+        hi += (h & 2u) ? 1 : -1;
+        lo = lo > 7 ? 6 : (lo < -7 ? -6 : lo);
+        hi = hi > 7 ? 6 : (hi < -7 ? -6 : hi);
+        dvc[i] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+    }
+    for (size_t i = i0; i < nks; i += stride) dks[i] = ks[i];
+    for (size_t i = i0; i < nvs; i += stride) dvs[i] = vs[i];
+}
+
+// bf16 queries, uniform on (-1.73, 1.73) (unit variance).
+__global__ void fill_bf16_kernel(uint16_t* q, size_t n, uint64_t seed) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = (unit_float(mix32(seed ^ i)) * 2.0f - 1.0f) * 1.7320508f;
+        q[i] = (uint16_t)(__float_as_uint(x) >> 16);
+    }
+}
+
+// ---- host side --------------------------------------------------------------
+
+struct Shape {
+    std::string name;
+    int n_draft;       // 1 for decode
+    int ctx;           // cached tokens (drafts included for verify)
+    bool small;
+};
+
+struct Cand {
+    q8k4v_config cfg;
+    std::string stage;             // "default", "structural", "refine"
+    std::string verdict;           // "admitted", "rejected", "invalid", "unknown"
+    std::string why;
+    double t[2] = {0, 0};          // median microseconds per shape
+    double dev[2] = {0, 0};        // max |out - default out| per shape
+    double ref_dev = -1;
+    double cost = 0;
+};
+
+struct Arena {
+    std::vector<void*> ptrs;
+    ~Arena() {
+        for (void* p : ptrs) (void)hipFree(p);
+    }
+    void* alloc(size_t bytes) {
+        void* p = nullptr;
+        if (hipMalloc(&p, std::max<size_t>(bytes, 256)) != hipSuccess) return nullptr;
+        ptrs.push_back(p);
+        return p;
+    }
+};
+
+std::string cfg_json(const q8k4v_config& c) {
+    char b[256];
+    std::snprintf(b, sizeof b,
+                  "{\"variant\":%d,\"waves_per_wg\":%d,\"wgs_per_cu\":%d,\"split_pages\":%d,\"fused_combine\":%d}",
+                  c.variant, c.waves_per_wg, c.wgs_per_cu, c.split_pages, c.fused_combine);
+    return b;
+}
+
+bool same_cfg(const q8k4v_config& a, const q8k4v_config& b) {
+    return a.variant == b.variant && a.waves_per_wg == b.waves_per_wg && a.wgs_per_cu == b.wgs_per_cu &&
+           a.split_pages == b.split_pages && a.fused_combine == b.fused_combine;
+}
+
+std::string fmt(double x) {
+    if (!std::isfinite(x)) return "null";     // JSON has no inf / nan
+    char b[64];
+    std::snprintf(b, sizeof b, "%.6g", x);
+    return b;
+}
+
+class Tuner {
+  public:
+    Tuner(const q8k4v_tune_request& r, Clock::time_point deadline) : req_(r), deadline_(deadline) {}
+
+    int32_t run(q8k4v_config* out_table, std::string* report);
+
+  private:
+    bool expired() const { return Clock::now() >= deadline_; }
+    int32_t setup(std::string* why);
+    int32_t launch(const q8k4v_config* cfg, const Shape& s, int copy, int set, float* out, const void* q);
+    int32_t time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us);
+    int32_t output(const q8k4v_config* cfg, const Shape& s, int copy, std::vector<float>* host);
+    int32_t ref_output(const q8k4v_config* cfg, bool verify, std::vector<float>* host);
+    void tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, bool* qualified);
+    void measure(int unit, Cand* c);
+
+    const q8k4v_tune_request& req_;
+    Clock::time_point deadline_;
+    Arena arena_;
+    hipStream_t stream_ = nullptr;
+    std::vector<hipEvent_t> events_;
+    int hq_ = 0, h_ = 0, d_ = 0, w_ = 0, g_ = 0;
+    float scale_ = 0;
+    int pages_ = 0, small_pages_ = 0, n_copies_ = 0, n_sets_ = 0, reps_ = 0;
+    uint64_t rot_ = 0;                   // rolling rotation counter
+    size_t cache_bytes_ = 0;
+    std::vector<q8k4v_cache> copies_;
+    int32_t* d_tables_ = nullptr;        // [n_sets][pages]: set 0 is the full permutation
+    int32_t* d_lens_ = nullptr;          // [4]: decode small, decode large, verify small, verify large
+    int32_t* d_ref_len_ = nullptr;       // [1]: the caller's reference length
+    void* d_q_ = nullptr;                // bf16 [w][hq][d]
+    float* d_out_ = nullptr;             // fp32 [w][hq][d]
+    void* d_ws_ = nullptr;
+    size_t ws_bytes_ = 0;
+    Shape shapes_[2][2];                 // [unit][small/large]
+    std::vector<float> def_out_[2][2];   // default outputs per unit/shape on copy 0
+    double noise_[2][2] = {{0, 0}, {0, 0}};
+    double def_t_[2][2] = {{0, 0}, {0, 0}};
+    std::vector<float> ref_host_[2];
+    std::string setup_note_;
+    std::string summary_, error_;
+
+  public:
+    const std::string& summary() const { return summary_; }
+    const std::string& error() const { return error_; }
+};
+
+int32_t Tuner::setup(std::string* why) {
+    hq_ = req_.num_q_heads;
+    h_ = req_.num_kv_heads;
+    d_ = req_.head_dim;
+    w_ = req_.n_draft;
+    g_ = hq_ / h_;
+    scale_ = req_.softmax_scale > 0 ? req_.softmax_scale : 1.0f / std::sqrt((float)d_);
+    const int ctx_s = req_.ctx_small, ctx_l = req_.ctx_large;
+    pages_ = (ctx_l + w_ + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE;
+    small_pages_ = (ctx_s + w_ + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE;
+    n_sets_ = std::max(1, pages_ / small_pages_);
+    const size_t per_th = (size_t)d_ + 2 + d_ / 2 + 2 * (d_ / 32);
+    cache_bytes_ = (size_t)pages_ * h_ * Q8K4V_PAGE_SIZE * per_th;
+    const int want = std::max(2, (int)((4 * kLlcBytes + cache_bytes_ - 1) / cache_bytes_) + 1);
+
+    shapes_[0][0] = {"decode@" + std::to_string(ctx_s), 1, ctx_s, true};
+    shapes_[0][1] = {"decode@" + std::to_string(ctx_l), 1, ctx_l, false};
+    shapes_[1][0] = {"verify@" + std::to_string(ctx_s) + "+" + std::to_string(w_), w_, ctx_s + w_, true};
+    shapes_[1][1] = {"verify@" + std::to_string(ctx_l) + "+" + std::to_string(w_), w_, ctx_l + w_, false};
+
+    // workspace: the largest any candidate can ask for (split count is capped
+    // by the combine, so the bound is the cap times the row records)
+    ws_bytes_ = 0;
+    for (int unit = 0; unit < 2; ++unit)
+        for (int wgs : {1, 2, 3, 4, 5, 6, 8, 12})
+            for (int waves : {1, 2, 4})
+                for (int variant : {0, 1, 2, 3}) {
+                    q8k4v_config c = default_config(unit == 1);
+                    c.wgs_per_cu = wgs;
+                    c.waves_per_wg = waves;
+                    c.variant = variant;
+                    c.fused_combine = 1;
+                    const int nd = unit ? w_ : 1;
+                    ws_bytes_ = std::max(ws_bytes_, q8k4v_workspace_bytes(1, hq_, h_, d_, ctx_l + w_, nd, &c));
+                }
+    ws_bytes_ = std::max<size_t>(ws_bytes_, 4096);
+
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: hipMemGetInfo");
+    const size_t cap = req_.mem_cap_bytes ? std::min(req_.mem_cap_bytes, free_b) : free_b;
+    const size_t fixed = ws_bytes_ + (size_t)n_sets_ * pages_ * 4 + (size_t)w_ * hq_ * d_ * 6 + (64u << 20);
+    int copies = want;
+    while (copies >= 2 && fixed + (size_t)copies * cache_bytes_ > cap) --copies;
+    if (copies < 2) {
+        *why = "memory admission: two cache copies of " + std::to_string(cache_bytes_) + " bytes do not fit in " +
+               std::to_string(cap) + " bytes";
+        return Q8K4V_ENOMEM;
+    }
+    if (copies < want) setup_note_ = "rotation limited by memory: " + std::to_string(copies) + " of " + std::to_string(want) + " copies";
+    n_copies_ = copies;
+
+    if (hipStreamCreateWithFlags(&stream_, hipStreamNonBlocking) != hipSuccess)
+        return hip_fail(hipGetLastError(), "tune_select: stream");
+    const size_t nk = (size_t)pages_ * h_ * 16 * d_, nks = (size_t)pages_ * h_ * 16;
+    const size_t nv = (size_t)pages_ * h_ * d_ * 8, nvs = (size_t)pages_ * h_ * 16 * (d_ / 32);
+    copies_.resize(n_copies_);
+    for (int i = 0; i < n_copies_; ++i) {
+        q8k4v_cache& c = copies_[i];
+        c.num_pages = pages_;
+        c.num_kv_heads = h_;
+        c.head_dim = d_;
+        c.page_size = Q8K4V_PAGE_SIZE;
+        c.k_codes = (int8_t*)arena_.alloc(nk);
+        c.k_scales = (uint16_t*)arena_.alloc(nks * 2);
+        c.v_codes = (uint8_t*)arena_.alloc(nv);
+        c.v_scales = (uint16_t*)arena_.alloc(nvs * 2);
+        if (!c.k_codes || !c.k_scales || !c.v_codes || !c.v_scales) {
+            *why = "hipMalloc of a cache copy failed";
+            return Q8K4V_ENOMEM;
+        }
+        if (i == 1) {   // copy 1: copy 0 with every code moved one step
+            hipLaunchKernelGGL(perturb_cache_kernel, dim3(2048), dim3(256), 0, stream_, copies_[0].k_codes,
+                               copies_[0].k_scales, copies_[0].v_codes, copies_[0].v_scales, c.k_codes, c.k_scales,
+                               c.v_codes, c.v_scales, nk, nks, nv, nvs, req_.seed ^ 0x5eedULL);
+        } else {
+            hipLaunchKernelGGL(fill_cache_kernel, dim3(2048), dim3(256), 0, stream_, c.k_codes, c.k_scales, c.v_codes,
+                               c.v_scales, nk, nks, nv, nvs, req_.seed * 1000003ULL + (uint64_t)i);
+        }
+        if (hipGetLastError() != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: fill");
+        if (expired()) return Q8K4V_OK;
+    }
+    // page tables: a seeded permutation of the pool; set j of the small
+    // context uses pages j*small_pages .. of it (disjoint sets)
+    std::vector<int32_t> perm(pages_);
+    for (int i = 0; i < pages_; ++i) perm[i] = i;
+    uint64_t s = req_.seed * 6364136223846793005ULL + 1442695040888963407ULL;
+    for (int i = pages_ - 1; i > 0; --i) {
+        s = s * 6364136223846793005ULL + 1442695040888963407ULL;
+        const int j = (int)((s >> 33) % (uint64_t)(i + 1));
+        std::swap(perm[i], perm[j]);
+    }
+    std::vector<int32_t> tables((size_t)n_sets_ * pages_);
+    for (int set = 0; set < n_sets_; ++set)
+        for (int i = 0; i < pages_; ++i)
+            tables[(size_t)set * pages_ + i] = perm[(i + (size_t)set * small_pages_) % pages_];
+    d_tables_ = (int32_t*)arena_.alloc(tables.size() * 4);
+    d_lens_ = (int32_t*)arena_.alloc(16);
+    d_q_ = arena_.alloc((size_t)w_ * hq_ * d_ * 2);
+    d_out_ = (float*)arena_.alloc((size_t)w_ * hq_ * d_ * 4);
+    d_ws_ = arena_.alloc(ws_bytes_);
+    if (!d_tables_ || !d_lens_ || !d_q_ || !d_out_ || !d_ws_) {
+        *why = "hipMalloc failed";
+        return Q8K4V_ENOMEM;
+    }
+    const int32_t lens[4] = {shapes_[0][0].ctx, shapes_[0][1].ctx, shapes_[1][0].ctx, shapes_[1][1].ctx};
+    if (hipMemcpyAsync(d_tables_, tables.data(), tables.size() * 4, hipMemcpyHostToDevice, stream_) != hipSuccess ||
+        hipMemcpyAsync(d_lens_, lens, sizeof lens, hipMemcpyHostToDevice, stream_) != hipSuccess)
+        return hip_fail(hipGetLastError(), "tune_select: upload");
+    hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream_, (uint16_t*)d_q_, (size_t)w_ * hq_ * d_,
+                       req_.seed ^ 0xA11CEULL);
+    // the fused combine's counters start at zero and reset themselves
+    if (hipMemsetAsync(d_ws_, 0, ws_bytes_, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
+    if (hipStreamSynchronize(stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: synthesis");
+    reps_ = 24;
+    events_.resize(2 * reps_);
+    for (auto& e : events_)
+        if (hipEventCreate(&e) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: events");
+    return Q8K4V_OK;
+}
+
+int32_t Tuner::launch(const q8k4v_config* cfg, const Shape& s, int copy, int set, float* out, const void* q) {
+    const int32_t* lens = d_lens_ + (s.n_draft > 1 ? 2 : 0) + (s.small ? 0 : 1);
+    const int32_t* table = d_tables_ + (size_t)(s.small ? set : 0) * pages_;
+    if (s.n_draft > 1)
+        return attn_verify_q8k4v(&copies_[copy], q, Q8K4V_BF16, out, 1, hq_, s.n_draft, lens, s.ctx, table, pages_,
+                                 scale_, cfg, d_ws_, ws_bytes_, stream_);
+    return attn_decode_q8k4v(&copies_[copy], q, Q8K4V_BF16, out, 1, hq_, lens, s.ctx, table, pages_, scale_, cfg,
+                             d_ws_, ws_bytes_, stream_);
+}
+
+int32_t Tuner::time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us) {
+    // two untimed launches, then reps_ single launches, each on the next copy
+    // copies are taken in a rolling order across all measurements, so a copy
+    // comes back only after every other copy (> 4x the LLC) has been read
+    for (int r = 0; r < 2; ++r) {
+        const int32_t rc = launch(cfg, s, (int)(rot_++ % n_copies_), 0, d_out_, d_q_);
+        if (rc != Q8K4V_OK) return rc;
+    }
+    for (int r = 0; r < reps_; ++r) {
+        const uint64_t k = rot_++;
+        const int copy = (int)(k % n_copies_);
+        const int set = s.small ? (int)((k / n_copies_) % n_sets_) : 0;
+        if (hipEventRecord(events_[2 * r], stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: event");
+        const int32_t rc = launch(cfg, s, copy, set, d_out_, d_q_);
+        if (rc != Q8K4V_OK) return rc;
+        if (hipEventRecord(events_[2 * r + 1], stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: event");
+    }
+    if (hipStreamSynchronize(stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: timing");
+    std::vector<double> t(reps_);
+    for (int r = 0; r < reps_; ++r) {
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, events_[2 * r], events_[2 * r + 1]) != hipSuccess)
+            return hip_fail(hipGetLastError(), "tune_select: elapsed");
+        t[r] = ms * 1e3;
+    }
+    std::nth_element(t.begin(), t.begin() + reps_ / 2, t.end());
+    *median_us = t[reps_ / 2];
+    return Q8K4V_OK;
+}
+
+int32_t Tuner::output(const q8k4v_config* cfg, const Shape& s, int copy, std::vector<float>* host) {
+    const size_t n = (size_t)s.n_draft * hq_ * d_;
+    if (hipMemsetAsync(d_out_, 0xFF, n * 4, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
+    const int32_t rc = launch(cfg, s, copy, 0, d_out_, d_q_);
+    if (rc != Q8K4V_OK) return rc;
+    host->resize(n);
+    if (hipMemcpyAsync(host->data(), d_out_, n * 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+        return hip_fail(hipGetLastError(), "tune_select: readback");
+    return Q8K4V_OK;
+}
+
+int32_t Tuner::ref_output(const q8k4v_config* cfg, bool verify, std::vector<float>* host) {
+    const int nd = verify ? w_ : 1;
+    const size_t n = (size_t)nd * hq_ * d_;
+    const int32_t len = req_.ref_len;
+    if (!d_ref_len_) {
+        d_ref_len_ = (int32_t*)arena_.alloc(4);
+        if (!d_ref_len_) return fail(Q8K4V_ENOMEM, "tune_select: hipMalloc");
+        if (hipMemcpyAsync(d_ref_len_, &len, 4, hipMemcpyHostToDevice, stream_) != hipSuccess ||
+            hipStreamSynchronize(stream_) != hipSuccess)
+            return hip_fail(hipGetLastError(), "tune_select: upload");
+    }
+    int32_t rc;
+    if (verify)
+        rc = attn_verify_q8k4v(req_.ref_cache, req_.ref_q_verify, Q8K4V_BF16, d_out_, 1, hq_, nd, d_ref_len_, len,
+                               req_.ref_page_table, req_.ref_max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
+    else
+        rc = attn_decode_q8k4v(req_.ref_cache, req_.ref_q, Q8K4V_BF16, d_out_, 1, hq_, d_ref_len_, len,
+                               req_.ref_page_table, req_.ref_max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
+    if (rc != Q8K4V_OK) return rc;
+    host->resize(n);
+    if (hipMemcpyAsync(host->data(), d_out_, n * 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+        return hip_fail(hipGetLastError(), "tune_select: readback");
+    return Q8K4V_OK;
+}
+
+double max_abs_diff(const std::vector<float>& a, const float* b, size_t n) {
+    double m = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const double d = std::fabs((double)a[i] - (double)b[i]);
+        if (!(d <= m)) m = std::isnan(d) ? INFINITY : d;
+    }
+    return m;
+}
+
+void Tuner::measure(int unit, Cand* c) {
+    // timing on both shapes, then the gate; "unknown" if the deadline passes
+    for (int k = 0; k < 2; ++k) {
+        if (expired()) { c->verdict = "unknown"; c->why = "deadline"; return; }
+        const int32_t rc = time_shape(&c->cfg, shapes_[unit][k], &c->t[k]);
+        if (rc != Q8K4V_OK) { c->verdict = "invalid"; c->why = q8k4v_last_error(); return; }
+    }
+    for (int k = 0; k < 2; ++k) {
+        if (expired()) { c->verdict = "unknown"; c->why = "deadline"; return; }
+        std::vector<float> o;
+        const int32_t rc = output(&c->cfg, shapes_[unit][k], 0, &o);
+        if (rc != Q8K4V_OK) { c->verdict = "invalid"; c->why = q8k4v_last_error(); return; }
+        c->dev[k] = max_abs_diff(def_out_[unit][k], o.data(), o.size());
+        if (!(c->dev[k] <= kAlpha * noise_[unit][k])) {
+            c->verdict = "rejected";
+            c->why = shapes_[unit][k].name + ": deviation " + fmt(c->dev[k]) + " > alpha * noise " +
+                     fmt(kAlpha * noise_[unit][k]);
+            return;
+        }
+    }
+    if (!ref_host_[unit].empty()) {
+        if (expired()) { c->verdict = "unknown"; c->why = "deadline"; return; }
+        std::vector<float> o;
+        const int32_t rc = ref_output(&c->cfg, unit == 1, &o);
+        if (rc != Q8K4V_OK) { c->verdict = "invalid"; c->why = q8k4v_last_error(); return; }
+        c->ref_dev = max_abs_diff(o, ref_host_[unit].data(), o.size());
+        if (!(c->ref_dev <= req_.ref_tol)) {
+            c->verdict = "rejected";
+            c->why = "reference deviation " + fmt(c->ref_dev) + " > ref_tol";
+            return;
+        }
+    }
+    c->cost = c->t[0] / def_t_[unit][0] + c->t[1] / def_t_[unit][1];
+    c->verdict = "admitted";
+}
+
+void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, bool* qualified) {
+    const int rows = (unit ? w_ : 1) * g_;
+    const bool dense = !(rows == 1 || rows == 2 || rows == 4 || rows == 8);
+    const q8k4v_config dflt = default_config(unit == 1);
+    *chosen = dflt;
+    *qualified = false;
+
+    // the default: its times normalise the cost; its outputs are the gate
+    Cand d;
+    d.cfg = dflt;
+    d.stage = "default";
+    for (int k = 0; k < 2 && d.verdict.empty(); ++k) {
+        if (expired()) { d.verdict = "unknown"; d.why = "deadline"; break; }
+        int32_t rc = time_shape(&dflt, shapes_[unit][k], &def_t_[unit][k]);
+        std::vector<float> pert;
+        if (rc == Q8K4V_OK) rc = output(&dflt, shapes_[unit][k], 0, &def_out_[unit][k]);
+        if (rc == Q8K4V_OK) rc = output(&dflt, shapes_[unit][k], 1, &pert);
+        if (rc != Q8K4V_OK) { d.verdict = "invalid"; d.why = q8k4v_last_error(); break; }
+        double peak = 0;
+        for (float x : def_out_[unit][k]) peak = std::max(peak, (double)std::fabs(x));
+        noise_[unit][k] = std::max(max_abs_diff(def_out_[unit][k], pert.data(), pert.size()), 1e-6 * peak);
+        d.t[k] = def_t_[unit][k];
+    }
+    if (d.verdict.empty() && req_.ref_cache && (unit ? req_.ref_q_verify && req_.ref_out_verify : req_.ref_q && req_.ref_out)) {
+        const float* ref = unit ? req_.ref_out_verify : req_.ref_out;
+        const size_t n = (size_t)(unit ? w_ : 1) * hq_ * d_;
+        ref_host_[unit].assign(ref, ref + n);
+        std::vector<float> o;
+        if (ref_output(&dflt, unit == 1, &o) != Q8K4V_OK) { d.verdict = "invalid"; d.why = q8k4v_last_error(); }
+        else d.ref_dev = max_abs_diff(o, ref_host_[unit].data(), n);
+    }
+    if (d.verdict.empty()) {
+        d.cost = 2.0;
+        d.verdict = (d.ref_dev < 0 || d.ref_dev <= req_.ref_tol) ? "admitted" : "rejected";
+        if (d.verdict == "rejected") d.why = "reference deviation " + fmt(d.ref_dev) + " > ref_tol";
+    }
+    cands->push_back(d);
+    // nothing is searched when the default itself is unmeasured, invalid or
+    // fails the caller's references: its times and outputs are the yardstick
+    if (d.verdict != "admitted") return;
+    size_t best_i = cands->size() - 1;
+    const int limit = req_.max_candidates > 0 ? req_.max_candidates : (1 << 20);
+    auto consider = [&](const q8k4v_config& c, const char* stage) {
+        for (const auto& e : *cands)
+            if (same_cfg(e.cfg, c)) return;
+        if ((int)cands->size() >= limit) return;
+        Cand x;
+        x.cfg = c;
+        x.stage = stage;
+        measure(unit, &x);
+        cands->push_back(x);
+        if (x.verdict == "admitted" && x.cost < (*cands)[best_i].cost) best_i = cands->size() - 1;
+    };
+    // structural variants: which kernel runs the unit
+    std::vector<int> variants;
+    if (dense) variants = {3};
+    else if (rows <= 2) variants = {1};
+    else variants = {2, 1};
+    for (int v : variants) {
+        q8k4v_config c = dflt;
+        c.variant = v;
+        consider(c, "structural");
+    }
+    // refinement of the launch shape around the best structural choice
+    const int base_variant = (*cands)[best_i].cfg.variant;
+    for (int fused : {0, 1})
+        for (int waves : {2, 4, 1})
+            for (int wgs : {5, 4, 6, 3, 8, 2, 12, 1}) {
+                q8k4v_config c = dflt;
+                c.variant = base_variant;
+                c.waves_per_wg = waves;
+                c.wgs_per_cu = wgs;
+                c.fused_combine = fused;
+                consider(c, "refine");
+            }
+    const Cand& b = (*cands)[best_i];
+    *chosen = b.cfg;
+    *qualified = b.verdict == "admitted";
+}
+
+int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
+    const auto t0 = Clock::now();
+    out_table[0] = default_config(false);
+    out_table[1] = default_config(true);
+    std::string why;
+    int32_t rc = setup(&why);
+    std::vector<Cand> cands[2];
+    q8k4v_config chosen[2] = {out_table[0], out_table[1]};
+    bool qual[2] = {false, false};
+    bool searched = false;
+    if (rc == Q8K4V_OK && !expired()) {
+        searched = true;
+        for (int unit = 0; unit < 2; ++unit) tune_unit(unit, &cands[unit], &chosen[unit], &qual[unit]);
+    }
+    for (int unit = 0; unit < 2; ++unit) {
+        out_table[unit] = chosen[unit];
+        out_table[unit].qualified = qual[unit] ? 1 : 0;
+        if (!qual[unit]) {
+            out_table[unit] = default_config(unit == 1);
+            out_table[unit].qualified = 0;
+        }
+    }
+    bool install = false;
+    if (req_.install && rc == Q8K4V_OK)
+        for (int unit = 0; unit < 2; ++unit)
+            if (qual[unit]) {
+                tuned_install(unit ? w_ : 1, hq_, h_, d_, out_table[unit]);
+                install = true;
+            }
+    const double elapsed = std::chrono::duration<double, std::milli>(Clock::now() - t0).count();
+
+    std::string j = "{";
+    j += "\"status\":\"" + std::string(searched ? "searched" : "defaults") + "\"";
+    j += ",\"budget_ms\":" + std::to_string(std::min<int64_t>(req_.budget_ms, kMaxBudgetMs));
+    j += ",\"elapsed_ms\":" + fmt(elapsed);
+    j += ",\"alpha\":" + fmt(kAlpha);
+    if (!why.empty()) j += ",\"error\":\"" + why + "\"";
+    j += ",\"rotation\":{\"copies\":" + std::to_string(n_copies_) + ",\"copy_bytes\":" + std::to_string(cache_bytes_) +
+         ",\"small_page_sets\":" + std::to_string(n_sets_) + ",\"llc_multiple\":" +
+         fmt((double)n_copies_ * cache_bytes_ / (double)kLlcBytes) + ",\"launches_per_median\":" + std::to_string(reps_) + "}";
+    if (!setup_note_.empty()) j += ",\"note\":\"" + setup_note_ + "\"";
+    j += ",\"installed\":" + std::string(install ? "true" : "false");
+    j += ",\"units\":[";
+    std::string cand_lists;
+    for (int unit = 0; unit < 2; ++unit) {
+        if (unit) j += ",";
+        int n_adm = 0, n_rej = 0, n_unk = 0, n_inv = 0;
+        for (const auto& c : cands[unit]) {
+            n_adm += c.verdict == "admitted";
+            n_rej += c.verdict == "rejected";
+            n_unk += c.verdict == "unknown";
+            n_inv += c.verdict == "invalid";
+        }
+        j += "{\"unit\":\"" + std::string(unit ? "verify" : "decode") + "\"";
+        j += ",\"rows_per_kv_head\":" + std::to_string((unit ? w_ : 1) * g_);
+        j += ",\"shapes\":[\"" + shapes_[unit][0].name + "\",\"" + shapes_[unit][1].name + "\"]";
+        j += ",\"default_us\":[" + fmt(def_t_[unit][0]) + "," + fmt(def_t_[unit][1]) + "]";
+        j += ",\"noise\":[" + fmt(noise_[unit][0]) + "," + fmt(noise_[unit][1]) + "]";
+        j += ",\"searched\":" + std::to_string(cands[unit].size());
+        j += ",\"admitted\":" + std::to_string(n_adm) + ",\"rejected\":" + std::to_string(n_rej) +
+             ",\"unknown\":" + std::to_string(n_unk) + ",\"invalid\":" + std::to_string(n_inv);
+        j += ",\"qualified\":" + std::string(qual[unit] ? "true" : "false");
+        j += ",\"chosen\":" + cfg_json(out_table[unit]);
+        double best_cost = 2.0, best_t0 = def_t_[unit][0], best_t1 = def_t_[unit][1];
+        for (const auto& c : cands[unit])
+            if (c.verdict == "admitted" && same_cfg(c.cfg, out_table[unit])) { best_cost = c.cost; best_t0 = c.t[0]; best_t1 = c.t[1]; }
+        j += ",\"chosen_cost\":" + fmt(best_cost) + ",\"chosen_us\":[" + fmt(best_t0) + "," + fmt(best_t1) + "]";
+        j += "}";
+        cand_lists += unit ? ",[" : "[";
+        for (size_t i = 0; i < cands[unit].size(); ++i) {
+            const Cand& c = cands[unit][i];
+            if (i) cand_lists += ",";
+            cand_lists += "{\"stage\":\"" + c.stage + "\",\"cfg\":" + cfg_json(c.cfg) + ",\"verdict\":\"" + c.verdict +
+                          "\",\"us\":[" + fmt(c.t[0]) + "," + fmt(c.t[1]) + "],\"dev\":[" + fmt(c.dev[0]) + "," +
+                          fmt(c.dev[1]) + "],\"cost\":" + fmt(c.cost);
+            if (c.ref_dev >= 0) cand_lists += ",\"ref_dev\":" + fmt(c.ref_dev);
+            if (!c.why.empty()) {
+                std::string w = c.why;
+                for (auto& ch : w)
+                    if (ch == '"' || ch == '\\' || (unsigned char)ch < 32) ch = ' ';
+                cand_lists += ",\"why\":\"" + w + "\"";
+            }
+            cand_lists += "}";
+        }
+        cand_lists += "]";
+    }
+    j += "]";
+    *report = j + ",\"candidates\":[" + cand_lists + "]}";
+    summary_ = j + "}";        // for a caller buffer too small for the candidate list
+    error_ = why;
+
+    for (auto& e : events_) (void)hipEventDestroy(e);
+    events_.clear();
+    if (stream_) {
+        (void)hipStreamSynchronize(stream_);
+        (void)hipStreamDestroy(stream_);
+        stream_ = nullptr;
+    }
+    return rc == Q8K4V_ENOMEM ? Q8K4V_ENOMEM : (rc == Q8K4V_OK ? Q8K4V_OK : rc);
+}
+
+}  // namespace
+}  // namespace q8k4v
 
 using namespace q8k4v;
 
 extern "C" int32_t tune_select(const q8k4v_tune_request* req, q8k4v_config* out_table, char* report_json,
                                size_t report_cap) {
+    const auto t0 = Clock::now();
     if (!req || !out_table) return fail(Q8K4V_EINVAL, "tune_select: NULL argument");
-    out_table[0] = default_config(false);
-    out_table[1] = default_config(true);
-    if (report_json && report_cap) std::snprintf(report_json, report_cap, "{\"searched\":0}");
-    return Q8K4V_OK;
+    if (req->num_kv_heads < 1 || req->num_q_heads < 1 || req->num_q_heads % req->num_kv_heads)
+        return fail(Q8K4V_EINVAL, "tune_select: num_q_heads must be a positive multiple of num_kv_heads");
+    const int g = req->num_q_heads / req->num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return fail(Q8K4V_EUNSUPPORTED, "tune_select: group must be 1, 2, 4 or 8");
+    if (req->head_dim != 64 && req->head_dim != 128) return fail(Q8K4V_EINVAL, "tune_select: head_dim must be 64 or 128");
+    if (req->n_draft < 1 || req->n_draft > Q8K4V_MAX_DRAFT) return fail(Q8K4V_EINVAL, "tune_select: n_draft must be in 1..16");
+    if (req->ctx_small < 1 || req->ctx_large < req->ctx_small)
+        return fail(Q8K4V_EINVAL, "tune_select: need 1 <= ctx_small <= ctx_large");
+    if (req->ref_cache && (req->ref_len < req->n_draft || !req->ref_page_table || req->ref_max_pages < 1 ||
+                           (int64_t)req->ref_max_pages * Q8K4V_PAGE_SIZE < req->ref_len))
+        return fail(Q8K4V_EINVAL, "tune_select: inconsistent reference inputs");
+    const int64_t budget = std::max<int64_t>(0, std::min<int64_t>(req->budget_ms, kMaxBudgetMs));
+    Tuner t(*req, t0 + std::chrono::milliseconds(budget));
+    std::string report;
+    const int32_t rc = t.run(out_table, &report);
+    if (report_json && report_cap) {
+        const std::string& r = report.size() < report_cap ? report : t.summary();
+        std::snprintf(report_json, report_cap, "%s", r.c_str());
+    }
+    if (rc == Q8K4V_ENOMEM) return fail(Q8K4V_ENOMEM, "tune_select: " + t.error());
+    return rc;
 }

@@ -230,8 +230,10 @@ typedef struct q8k4v_tune_request {
     int64_t budget_ms;                 /* wall clock, clamped to 60000 */
     size_t  mem_cap_bytes;             /* 0: free device memory at the call */
     uint64_t seed;                     /* synthetic cache contents */
-    int32_t install;                   /* 1: winners become the defaults used when cfg == NULL
-                                          for this (heads, head_dim) shape */
+    int32_t install;                   /* 1: qualified winners become the configuration used
+                                          when cfg == NULL, on this device, for this
+                                          (n_draft, num_q_heads, num_kv_heads, head_dim);
+                                          the decode unit is stored under n_draft 1 */
     int32_t max_candidates;            /* 0: no limit */
     /* optional gate against caller references on caller inputs (may be NULL):
        ref_cache + ref_q/ref_out for decode at ref_len (one sequence) */

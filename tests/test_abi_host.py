@@ -95,3 +95,22 @@ def test_workspace_size_follows_the_plan(lib):
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, cfg) == 0     # one split: direct write
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(waves_per_wg=3)) == 0  # invalid config
     assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(variant=2)) == 0  # 1 row: no block MFMA
+
+
+def test_tuner_rejects_bad_requests(lib):
+    """tune_select validates the request before touching the device."""
+    def tune(**kw):
+        r = q8.TuneRequest()
+        base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, n_draft=8, ctx_small=4096, ctx_large=65536,
+                    budget_ms=1000)
+        for k, v in {**base, **kw}.items():
+            setattr(r, k, v)
+        table = (q8.Config * 2)()
+        return lib.tune_select(C.byref(r), table, None, 0)
+    assert tune(num_q_heads=30) == -1           # not a multiple of the kv heads
+    assert tune(num_q_heads=24) == -2           # group 3
+    assert tune(head_dim=96) == -1
+    assert tune(n_draft=0) == -1 and tune(n_draft=17) == -1
+    assert tune(ctx_small=0) == -1
+    assert tune(ctx_small=8192, ctx_large=4096) == -1
+    assert lib.tune_select(None, None, None, 0) == -1
