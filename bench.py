@@ -46,11 +46,13 @@ def parse():
                     choices=["gqa_decode_65536", "gqa_decode_4096", "verify_65536_w8", "multi_session_16x32768"])
     ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0: enough for 4x LLC)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps", type=int, default=20)
     ap.add_argument("--tune", action="store_true", help="run tune_select first and use its choice")
     ap.add_argument("--config", default="", help="JSON dict of launch config fields")
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention launches (profiling)")
     ap.add_argument("--contiguous-pages", action="store_true", help="identity page table (profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -65,6 +67,8 @@ def main() -> int:
     import decode_attention_quantized_kv_amd as q8
     import workloads
 
+    if args.copy_calibration:
+        return copy_calibration(torch, args.copy_calibration)
     q8.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -207,9 +211,10 @@ def main() -> int:
                    "rotating_layer_caches": layers, "layer_cache_bytes": layer_bytes,
                    "launch_config": tuned or (cfg.as_dict() if cfg else "default")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attention (split-K attention kernel + combine)", "algorithmic_bytes": attn_bytes,
-                     "avg_launch_us": round(ms_attn * 1e3, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(w.name, nd),
+                     "kernel": ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v")
+                               + " launch (split-K attention kernel + LSE combine kernel)",
+                     "algorithmic_bytes": attn_bytes, "avg_launch_us": round(ms_attn * 1e3, 3)},
         "step_bytes": step_bytes,
         "wall_s": round(wall, 3),
         "device": device_info(torch),
@@ -217,6 +222,53 @@ def main() -> int:
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_steps, step_bytes, tokens)
     print(json.dumps(res), flush=True)
+    return 0
+
+
+# Kernel sources whose HBM traffic the committed counter summary describes;
+# the summary is used only while these files are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    False: ["attn_bmfma.hip", "attn_valu.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp"],
+    True: ["attn_mfma.hip", "attn_bmfma.hip", "attn_valu.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp"],
+}
+
+
+def kernel_sources_sha(verify: bool) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_quantized_kv_amd", "csrc")
+    for name in KERNEL_SOURCES[verify]:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload: str, n_draft: int):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
+    counters, each scaled by what the same counter reads for a plain copy of
+    known size; None when absent or taken on other kernel sources."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+        e = t["workloads"][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("kernel_sources_sha") != kernel_sources_sha(bool(n_draft)):
+        return None
+    kib = e["fetch_kib"] * t["copy_factor"]["fetch"] + e["write_kib"] * t["copy_factor"]["write"]
+    return int(round(kib * 1024))
+
+
+def copy_calibration(torch, mib: int) -> int:
+    """Device-to-device copies of a known size: the reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
     return 0
 
 
