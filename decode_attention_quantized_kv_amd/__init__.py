@@ -45,10 +45,10 @@ class CacheDesc(C.Structure):
 class Config(C.Structure):
     _fields_ = [("wgs_per_cu", C.c_int32), ("split_pages", C.c_int32), ("tile_pages", C.c_int32),
                 ("waves_per_wg", C.c_int32), ("fused_combine", C.c_int32), ("qualified", C.c_int32),
-                ("variant", C.c_int32), ("reserved", C.c_int32)]
+                ("variant", C.c_int32), ("stages", C.c_int32)]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 class TuneRequest(C.Structure):

@@ -21,6 +21,7 @@ namespace q8k4v {
 int32_t launch_valu(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_bmfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_mfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
+int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
 
 namespace {
@@ -69,13 +70,27 @@ int32_t device_cu_count() {
     return cached[dev];
 }
 
-q8k4v_config default_config(bool verify) {
+namespace {
+bool dec2_rows(int32_t rows) { return rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16; }
+
+// launch shape defaults per kernel
+void kernel_defaults(int32_t kernel, q8k4v_config* c) {
+    switch (kernel) {
+        case kDec2: c->wgs_per_cu = 2; c->waves_per_wg = 4; c->stages = 3; c->tile_pages = 2; break;
+        case kMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 2; break;
+        case kBlockMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
+        default: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
+    }
+}
+
+int32_t auto_kernel(int32_t rows) { return dec2_rows(rows) ? kDec2 : kMfma; }
+}  // namespace
+
+q8k4v_config default_config(int32_t rows) {
     q8k4v_config c;
     std::memset(&c, 0, sizeof(c));
-    c.wgs_per_cu = 5;
+    kernel_defaults(auto_kernel(rows), &c);
     c.split_pages = 0;
-    c.tile_pages = verify ? 2 : 4;
-    c.waves_per_wg = 2;
     c.fused_combine = 0;
     c.qualified = 0;
     c.variant = 0;
@@ -127,41 +142,53 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     (void)D;
 
     const int32_t rows = a.n_draft * G;
-    // 1, 2, 4 or 8 rows per kv head fit the vector and block-MFMA kernels;
-    // any other row count goes to the dense-MFMA kernel (masked to 16/32 rows)
-    const bool dense = rows != 1 && rows != 2 && rows != 4 && rows != 8;
     q8k4v_config cfg;
     if (cfg_in) cfg = *cfg_in;
-    else if (!tuned_lookup(a.n_draft, a.num_q_heads, H, D, &cfg)) cfg = default_config(a.n_draft > 1);
-    const q8k4v_config dflt = default_config(a.n_draft > 1);
-    if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = dflt.wgs_per_cu;
-    if (cfg.tile_pages <= 0) cfg.tile_pages = dflt.tile_pages;
-    if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = dflt.waves_per_wg;
-    if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4)
-        return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
+    else if (!tuned_lookup(a.n_draft, a.num_q_heads, H, D, &cfg)) cfg = default_config(rows);
 
     int32_t kernel;
-    if (dense) {
-        if (cfg.variant != 0 && cfg.variant != 3) return fail(Q8K4V_EINVAL, "attention: row counts other than 1, 2, 4, 8 need variant 0 or 3");
-        kernel = kMfma;
-    } else if (cfg.variant == 1 || rows <= 2) {
-        if (cfg.variant != 0 && cfg.variant != 1) return fail(Q8K4V_EINVAL, "attention: 1 or 2 rows need variant 0 or 1");
-        kernel = kVector;
-    } else {
-        if (cfg.variant != 0 && cfg.variant != 2) return fail(Q8K4V_EINVAL, "attention: 4 or 8 rows need variant 0, 1 or 2");
-        kernel = kBlockMfma;
+    switch (cfg.variant) {
+        case 0: kernel = auto_kernel(rows); break;
+        case 1:
+            if (rows != 1 && rows != 2 && rows != 4 && rows != 8)
+                return fail(Q8K4V_EINVAL, "attention: variant 1 needs 1, 2, 4 or 8 rows per kv head");
+            kernel = kVector;
+            break;
+        case 2:
+            if (rows != 4 && rows != 8) return fail(Q8K4V_EINVAL, "attention: variant 2 needs 4 or 8 rows per kv head");
+            kernel = kBlockMfma;
+            break;
+        case 3: kernel = kMfma; break;
+        case 4:
+            if (!dec2_rows(rows)) return fail(Q8K4V_EINVAL, "attention: variant 4 needs 1, 2, 4, 8 or 16 rows per kv head");
+            kernel = kDec2;
+            break;
+        default: return fail(Q8K4V_EINVAL, "attention: variant must be 0..4");
     }
-    // tile: the block-MFMA kernel works on 4-page tiles, the dense one on 2
+    q8k4v_config kd;
+    std::memset(&kd, 0, sizeof(kd));
+    kernel_defaults(kernel, &kd);
+    if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = kd.wgs_per_cu;
+    if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = kd.waves_per_wg;
+    if (cfg.stages <= 0) cfg.stages = kd.stages;
+    if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4)
+        return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
+    if (kernel == kDec2 && cfg.waves_per_wg == 1) return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2 or 4 waves");
+    if (kernel == kDec2 && cfg.stages != 2 && cfg.stages != 3) return fail(Q8K4V_EINVAL, "attention: stages must be 2 or 3");
+    // tiles: the MFMA kernels fix their tile length
     if (kernel == kBlockMfma) cfg.tile_pages = 4;
-    if (kernel == kMfma) cfg.tile_pages = 2;
+    else if (kernel == kMfma || kernel == kDec2) cfg.tile_pages = 2;
+    else if (cfg.tile_pages <= 0) cfg.tile_pages = kd.tile_pages;
     if (cfg.tile_pages != 1 && cfg.tile_pages != 2 && cfg.tile_pages != 4)
         return fail(Q8K4V_EINVAL, "attention: tile_pages must be 1, 2 or 4");
+    const bool dense = kernel == kMfma;
 
     plan->rows = rows;
     plan->kernel = kernel;
     plan->mfma = dense;
     plan->tile_pages = cfg.tile_pages;
     plan->waves = cfg.waves_per_wg;
+    plan->stages = cfg.stages;
     plan->rows_per_wg = (kernel == kMfma) ? (rows > 16 ? 32 : 16) : rows;
     plan->row_chunks = (rows + plan->rows_per_wg - 1) / plan->rows_per_wg;
     const int32_t max_np = std::max(1, (a.max_seq_len + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE);
@@ -176,6 +203,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);
     }
     sp = std::max(sp, unit);
+    if (kernel == kDec2) sp = std::min(sp, 64 * cfg.waves_per_wg);   // <= 64 pages per wave
     plan->split_pages = sp;
     plan->n_splits = (max_np + sp - 1) / sp;
     if (plan->n_splits > kCombineMaxSplits) {   // the combine holds one weight per split in LDS
@@ -183,6 +211,8 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         plan->split_pages = sp;
         plan->n_splits = (max_np + sp - 1) / sp;
     }
+    if (kernel == kDec2 && plan->split_pages > 64 * cfg.waves_per_wg)
+        return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long for variant 4 (more than 1024 splits)");
     plan->fused_combine = (plan->n_splits > 1 && cfg.fused_combine) ? 1 : 0;
     const size_t rec = (size_t)(a.cache->head_dim + 4) * sizeof(float);
     plan->partial_bytes = plan->n_splits > 1 ? (size_t)a.n_seqs * H * plan->n_splits * rows * rec : 0;
@@ -230,6 +260,7 @@ int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, s
     switch (plan.kernel) {
         case kVector: rc = launch_valu(kp, plan, c.head_dim, bf, stream); break;
         case kBlockMfma: rc = launch_bmfma(kp, plan, c.head_dim, bf, stream); break;
+        case kDec2: rc = launch_dec2(kp, plan, c.head_dim, bf, stream); break;
         default: rc = launch_mfma(kp, plan, c.head_dim, bf, stream); break;
     }
     if (rc != Q8K4V_OK) return rc;

@@ -1,0 +1,432 @@
+// Split-K attention over the paged k8v4 cache for 1 to 16 query rows per kv
+// head (a GQA group, or drafts x group), on gfx950's 16x16 MFMAs with the
+// query rows replicated across the MFMA columns.
+//
+// What it computes: exact softmax attention over the dequantized cache (the
+// decode unit of blog.123qwe.co.kr/?p=3927, section 5); row r = (draft j,
+// group member g) of sequence b sees positions 0 .. L_b - W + j.
+//
+// Layout of the work.  A workgroup owns a range of pages of one (sequence,
+// kv head); its waves take 2-page tiles round robin.  Each wave keeps a ring
+// of STAGES tile buffers in LDS filled by global_load_lds_dwordx4, so
+// STAGES - 1 tiles are in flight while one is computed; completion is tracked
+// with partial vmcnt waits.  The wave's page ids sit one per lane in a VGPR
+// (read with v_readlane when a tile is issued), so no table lookup is on the
+// critical path.
+//
+// Per tile (pages P0, P1; lane l = (n = l & 15, q = l >> 4)):
+//  * S^T = K Q^T on v_mfma_i32_16x16x64_i8, one instruction chain per page:
+//    the page's 16 tokens are the MFMA rows, the stored int8 key codes the A
+//    operand.  The B operand holds query row (n mod R) in column n, as a
+//    15-bit fixed-point number split into int8 halves (two chains, exact
+//    int32 sums).  Lane (n, q) receives the scores of row n mod R for tokens
+//    4q .. 4q+3 of the page;
+//  * online softmax per row in the log2 domain, reductions across the four
+//    lane groups with v_permlane16_swap / v_permlane32_swap (no LDS);
+//  * O = P' V on v_mfma_f32_16x16x32_f16: A row m is (query row m mod R, value
+//    group (m / R) mod NG) -- the lane already holds that row's
+//    probabilities, multiplies them by the token's value-group scale and
+//    rounds once to fp16; k = the 32 tokens of the tile (for lane group q:
+//    tokens 4q .. 4q+3 of P0 and of P1); B = the value codes as exact fp16
+//    (one 32-bit word per lane and output tile: 4 nibbles of P0, 4 of P1).
+//    Output tile dt (dims 16dt .. 16dt+15, value group dt/2) keeps the rows
+//    of its group.
+#include "attn_common.h"
+#include "q8k4v_internal.h"
+
+namespace q8k4v {
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+template <int N>
+Q8K4V_DEV void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+Q8K4V_DEV uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+Q8K4V_DEV float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// max / sum with the lanes 16 and 32 apart (the four lane groups)
+Q8K4V_DEV float xgroups_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+    x = fmaxf(bitsf(a[0]), bitsf(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    return fmaxf(bitsf(b[0]), bitsf(b[1]));
+}
+Q8K4V_DEV float xgroups_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+    x = bitsf(a[0]) + bitsf(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    return bitsf(b[0]) + bitsf(b[1]);
+}
+
+// 32-bit word of value codes -> four exact fp16 pairs: nibble j (bits
+// 4j..4j+3) and nibble j+4 (bits 16+4j..) become pair j.  One v_bitop3 per
+// pair copies the nibble's low three bits, inverts its top bit (two's
+// complement code -> code + 8) and sets the fp16 exponent of 1024: the pair
+// reads 1032 + code (nibble at bit 0 of a half) or 1152 + 16 code (nibble at
+// bit 4), and one packed add / fma returns the code exactly.
+// bitop3 truth table (sources x, A, B): x where A & ~B, ~x where ~A & B, 1
+// where A & B, 0 elsewhere -> 0xCA.
+Q8K4V_DEV uint32_t nib_to_f16(uint32_t x, uint32_t a, uint32_t b) { return __builtin_amdgcn_bitop3_b32(x, a, b, 0xCA); }
+
+Q8K4V_DEV void v_word_to_f16(uint32_t x, uint32_t out[4]) {
+    const uint32_t y = x >> 8;
+    const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const f16x2 inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const f16x2 off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    out[0] = as_u32(as_h2(nib_to_f16(x, 0x64076407u, 0x64086408u)) + off);
+    out[1] = as_u32(__builtin_elementwise_fma(as_h2(nib_to_f16(x, 0x64706470u, 0x64806480u)), inv16, off16));
+    out[2] = as_u32(as_h2(nib_to_f16(y, 0x64076407u, 0x64086408u)) + off);
+    out[3] = as_u32(__builtin_elementwise_fma(as_h2(nib_to_f16(y, 0x64706470u, 0x64806480u)), inv16, off16));
+}
+
+template <int D, int R, int WAVES, int STAGES, bool QBF16>
+__global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
+    constexpr int TP = 2;                      // pages per tile
+    constexpr int KB = 16 * D, VB = 8 * D;     // key / value code bytes per page
+    constexpr int NG = D / 32;                 // value groups
+    constexpr int KSB = 32, VSB = 32 * NG;     // scale bytes per page
+    constexpr int OFF_V = TP * KB, OFF_KS = OFF_V + TP * VB, OFF_VS = OFF_KS + TP * KSB;
+    constexpr int STAGE = OFF_VS + TP * VSB;   // 6464 B at D = 128
+    constexpr int CPR = D / 16;                // 16-byte chunks per key row
+    constexpr int KS = D / 64;                 // 64-dimension k-steps of q.K
+    constexpr int NDT = D / 16;                // 16-dimension output tiles
+    constexpr int NA = (R * NG + 15) / 16;     // A tiles of (row, group) pairs
+    constexpr int KI = KB / 1024;              // 1 KiB key copies per page
+    constexpr int IPT = TP * (KI + 3);         // copy instructions per tile
+    static_assert(16 % R == 0, "R must divide 16");
+    static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
+    static_assert(R * D * 4 <= STAGES * STAGE, "the merge buffer reuses the tile ring");
+
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES][STAGES][STAGE];
+    __shared__ float s_ml[WAVES][R][2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    WorkItem w;
+    if (!work_item(p, w)) return;
+    if (w.pbeg >= w.pend) {
+        if (w.split == 0) write_zero_rows<D>(p, w, 0, R);
+        return;
+    }
+    const int n16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int row = n16 % R;                   // query row of this lane's scores
+    const int kh = w.kh, pend = w.pend;
+    const int ntile_all = (pend - w.pbeg + TP - 1) / TP;
+    const int nt = ntile_all > wave ? (ntile_all - wave + WAVES - 1) / WAVES : 0;   // <= 32 (planner)
+
+    // page ids of this wave's tiles, one per lane: page u of wave tile t is
+    // lane 2t + u (pages past the split end repeat its last page; masked)
+    int my_id = 0;
+    {
+        const int pg = w.pbeg + TP * (wave + WAVES * (lane >> 1)) + (lane & 1);
+        if (lane < TP * nt) my_id = p.page_table[(size_t)w.b * p.max_pages + min(pg, pend - 1)];
+    }
+
+    uint8_t* const stage0 = &s_stage[wave][0][0];
+    const uint32_t lds0 = lds_addr(stage0);
+    uint32_t kdma_off[KI];                     // key rows swizzled: chunk c of row t at t*CPR + (c ^ t%CPR)
+#pragma unroll
+    for (int c = 0; c < KI; ++c) {
+        const int s = 64 * c + lane;
+        const int t = s / CPR, cc = (s % CPR) ^ (t % CPR);
+        kdma_off[c] = (uint32_t)(t * D + 16 * cc);
+    }
+    auto issue = [&](int t, int slot) {
+        const uint32_t base = lds0 + slot * STAGE;
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const int id = __builtin_amdgcn_readlane(my_id, TP * t + u);
+            const size_t blk = (size_t)id * p.H + kh;
+#pragma unroll
+            for (int c = 0; c < KI; ++c) lds_dma16(p.k_codes + blk * KB, kdma_off[c], base + u * KB + c * 1024);
+            if (VB >= 1024) {
+                lds_dma16(p.v_codes + blk * VB, lane * 16, base + OFF_V + u * VB);
+            } else if (lane < VB / 16) {
+                lds_dma16(p.v_codes + blk * VB, lane * 16, base + OFF_V + u * VB);
+            }
+            if (lane < 2) lds_dma16(p.k_scales + blk * 16, lane * 16, base + OFF_KS + u * KSB);
+            if (lane < 2 * NG) lds_dma16(p.v_scales + blk * 16 * NG, lane * 16, base + OFF_VS + u * VSB);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nt) issue(s, s);
+
+    // ---- query row (n mod R) as the B operand: 15-bit fixed point
+    // Q = rne(q * 2^(14-e)) (2^(e-1) <= max|q_row| < 2^e), int8 halves
+    // hi = (Q + 128) >> 8, lo = Q - 256 hi; lane (n, q) holds dims
+    // 64 ks + 16 q .. +15 of every k-step ks
+    u32x4 qhi[KS], qlo[KS];
+    float coef;
+    int lim;
+    {
+        const size_t qoff = out_index(p, w.b, kh, row, D);
+        float x[KS][16];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = 64 * ks + 16 * q4;
+            if (QBF16) {
+                const u32x4* src = (const u32x4*)((const uint16_t*)p.q + qoff + d0);
+                const u32x4 a = src[0], b = src[1];
+                const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    x[ks][2 * i] = bitsf(wd[i] << 16);
+                    x[ks][2 * i + 1] = bitsf(wd[i] & 0xFFFF0000u);
+                }
+            } else {
+                const f32x4* src = (const f32x4*)((const float*)p.q + qoff + d0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 v = src[i];
+                    x[ks][4 * i] = v.x; x[ks][4 * i + 1] = v.y; x[ks][4 * i + 2] = v.z; x[ks][4 * i + 3] = v.w;
+                }
+            }
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(x[ks][i]));
+        mx = xgroups_max(mx);
+        int e = 0;
+        if (mx > 0.0f) (void)frexpf(mx, &e);
+        e = min(max(e, -110), 110);
+        const float sc = ldexpf(1.0f, 14 - e);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint32_t h4 = 0, l4 = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int Q = (int)rintf(x[ks][4 * c + t] * sc);
+                    const int hi = (Q + 128) >> 8;
+                    h4 |= (uint32_t)(hi & 0xFF) << (8 * t);
+                    l4 |= (uint32_t)((Q - 256 * hi) & 0xFF) << (8 * t);
+                }
+                hw[c] = h4;
+                lw[c] = l4;
+            }
+            qhi[ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            qlo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        }
+        coef = p.scale_log2 * ldexpf(1.0f, e - 14);
+        lim = w.L - p.W + 1 + row / p.G;
+    }
+    const int lim_min = w.L - p.W + 1;         // every row sees the positions below this
+
+    float m_run = kNegInf, l_run = 0.0f;       // row `row`; l_run over this lane's tokens
+    f32x4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // value group of A row m = n16 in A tile a
+    int grp[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) grp[a] = ((16 * a + n16) / R) % NG;
+
+    for (int t = 0; t < nt; ++t) {
+        const int slot = t % STAGES;
+        if (t + STAGES - 1 < nt) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
+        const int after = min(STAGES - 1, nt - 1 - t);   // tiles issued after this one
+        if (STAGES == 3 && after >= 2) wait_vmem<2 * IPT>();
+        else if (after >= 1) wait_vmem<IPT>();
+        else wait_vmem<0>();
+
+        // ---- tile to registers
+        const uint8_t* st = stage0 + slot * STAGE;
+        u32x4 ka[TP][KS];
+#pragma unroll
+        for (int u = 0; u < TP; ++u)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = 4 * ks + q4;
+                ka[u][ks] = *(const u32x4*)(st + u * KB + (n16 * CPR + (c ^ (n16 % CPR))) * 16);
+            }
+        uint32_t vx[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int off = OFF_V + (16 * dt + n16) * 8 + 2 * q4;
+            vx[dt] = (uint32_t)*(const uint16_t*)(st + off) | ((uint32_t)*(const uint16_t*)(st + off + VB) << 16);
+        }
+        u32x2 ksw[TP];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) ksw[u] = *(const u32x2*)(st + OFF_KS + u * KSB + 8 * q4);
+        float vsf[NA][TP][4];                  // value scale of (group grp[a], page u, token 4q4 + j)
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int u = 0; u < TP; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    vsf[a][u][j] = h2f(*(const uint16_t*)(st + OFF_VS + u * VSB + ((4 * q4 + j) * NG + grp[a]) * 2));
+        wait_lds_all();
+
+        // ---- scores
+        i32x4_t chi[TP], clo[TP];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            chi[u] = i32x4_t{0, 0, 0, 0};
+            clo[u] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const i32x4_t a = __builtin_bit_cast(i32x4_t, ka[u][ks]);
+                chi[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qhi[ks]), chi[u], 0, 0, 0);
+                clo[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qlo[ks]), clo[u], 0, 0, 0);
+            }
+        }
+        const int pg0 = w.pbeg + TP * (wave + WAVES * t);
+        float s[TP][4];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const float kf[4] = {h2f((uint16_t)ksw[u].x), h2f((uint16_t)(ksw[u].x >> 16)), h2f((uint16_t)ksw[u].y),
+                                 h2f((uint16_t)(ksw[u].y >> 16))};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[u][i] = (float)(256 * chi[u][i] + clo[u][i]) * (kf[i] * coef);
+        }
+        if ((pg0 + TP) * 16 > lim_min || pg0 + TP > pend) {      // tile reaches the causal edge / split end
+#pragma unroll
+            for (int u = 0; u < TP; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = (pg0 + u) * 16 + 4 * q4 + i;
+                    if (!(pg0 + u < pend && pos < lim)) s[u][i] = kNegInf;
+                }
+        }
+        // ---- online softmax (row `row`)
+        float tmax = kNegInf;
+#pragma unroll
+        for (int u = 0; u < TP; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[u][i]);
+        tmax = xgroups_max(tmax);
+        const float m_new = fmaxf(m_run, tmax);
+        const float ref = (m_new == kNegInf) ? 0.0f : m_new;
+        const float alpha = exp2_fast(m_run - ref);
+        m_run = m_new;
+        float psum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < TP; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[u][i] = exp2_fast(s[u][i] - ref);
+                psum += s[u][i];
+            }
+        l_run = l_run * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(alpha < 1.0f) != 0) {
+            // output rows 4q4 + i hold query row (4q4 + i) mod R
+            float ai[4];
+            if (R <= 4) {
+                const int bits = __builtin_bit_cast(int, alpha);
+                ai[0] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(bits, 0x00, 0xF, 0xF, false));
+                ai[1] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(bits, 0x55, 0xF, 0xF, false));
+                ai[2] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(bits, 0xAA, 0xF, 0xF, false));
+                ai[3] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(bits, 0xFF, 0xF, 0xF, false));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, (4 * q4 + i) % R);
+            }
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                acc[dt][0] *= ai[0]; acc[dt][1] *= ai[1]; acc[dt][2] *= ai[2]; acc[dt][3] *= ai[3];
+            }
+        }
+        // ---- A operands: P' = p * value scale, rounded once to fp16; half
+        // 2j + u of the lane = page u, token 4q4 + j
+        u32x4 pa[NA];
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            uint32_t wd[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f16x2 h = __builtin_convertvector(
+                    (float __attribute__((ext_vector_type(2)))){s[0][j] * vsf[a][0][j], s[1][j] * vsf[a][1][j]}, f16x2);
+                wd[j] = as_u32(h);
+            }
+            pa[a] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+        }
+        // ---- O += P' V
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int a = ((dt / 2) * R) / 16;
+            uint32_t b[4];
+            v_word_to_f16(vx[dt], b);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, pa[a]),
+                                                              __builtin_bit_cast(f16x8_t, u32x4{b[0], b[1], b[2], b[3]}),
+                                                              acc[dt], 0, 0, 0);
+        }
+    }
+
+    // ---- per-wave state to LDS, merge the waves, emit
+    const float l_tot = xgroups_sum(l_run);
+    if (q4 == 0 && n16 < R) {
+        s_ml[wave][n16][0] = m_run;
+        s_ml[wave][n16][1] = l_tot;
+    }
+    __syncthreads();           // every wave is done with its ring: reuse it for O
+    float* s_o = (float*)&s_stage[0][0][0];   // [WAVES][R][D]
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int g = dt / 2;
+        const int a = (g * R) / 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * q4 + i;                 // C row in A tile a
+            const int idx = 16 * a + m;               // (row, group) index
+            if (idx >= g * R && idx < g * R + R)
+                s_o[(wave * R + idx % R) * D + 16 * dt + n16] = acc[dt][i];
+        }
+    }
+    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o);
+}
+
+template <int D, int R, int WAVES, int STAGES, bool QBF16>
+hipError_t launch_t(const AttnParams& kp, hipStream_t stream) {
+    const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
+    const int blocks = 8 * ((total + 7) / 8);
+    hipLaunchKernelGGL((attn_dec2_kernel<D, R, WAVES, STAGES, QBF16>), dim3(blocks), dim3(64 * WAVES), 0, stream, kp);
+    return hipGetLastError();
+}
+
+using LaunchFn = hipError_t (*)(const AttnParams&, hipStream_t);
+
+template <int D, int R, bool QBF16>
+LaunchFn pick_shape(int waves, int stages) {
+    if (waves == 2 && stages == 2) return &launch_t<D, R, 2, 2, QBF16>;
+    if (waves == 2 && stages == 3) return &launch_t<D, R, 2, 3, QBF16>;
+    if (waves == 4 && stages == 2) return &launch_t<D, R, 4, 2, QBF16>;
+    if (waves == 4 && stages == 3) return &launch_t<D, R, 4, 3, QBF16>;
+    return nullptr;
+}
+
+template <int D, bool QBF16>
+LaunchFn pick(int rows, int waves, int stages) {
+    switch (rows) {
+        case 1: return pick_shape<D, 1, QBF16>(waves, stages);
+        case 2: return pick_shape<D, 2, QBF16>(waves, stages);
+        case 4: return pick_shape<D, 4, QBF16>(waves, stages);
+        case 8: return pick_shape<D, 8, QBF16>(waves, stages);
+        case 16: return pick_shape<D, 16, QBF16>(waves, stages);
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
+    LaunchFn fn = nullptr;
+    if (head_dim == 128) fn = qbf16 ? pick<128, true>(plan.rows, plan.waves, plan.stages) : pick<128, false>(plan.rows, plan.waves, plan.stages);
+    else fn = qbf16 ? pick<64, true>(plan.rows, plan.waves, plan.stages) : pick<64, false>(plan.rows, plan.waves, plan.stages);
+    if (!fn) return fail(Q8K4V_EUNSUPPORTED, "attention: no paged-MFMA kernel for this rows/waves/stages combination");
+    const hipError_t e = fn(kp, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return Q8K4V_OK;
+}
+
+}  // namespace q8k4v

@@ -43,7 +43,7 @@ struct AttnArgs {
     float softmax_scale;
 };
 
-enum Kernel { kVector = 1, kBlockMfma = 2, kMfma = 3 };
+enum Kernel { kVector = 1, kBlockMfma = 2, kMfma = 3, kDec2 = 4 };
 
 // Fully resolved launch plan.
 struct Plan {
@@ -52,6 +52,7 @@ struct Plan {
     int32_t mfma;          // 1: the unit is the dense-MFMA one (more than 8 rows)
     int32_t tile_pages;
     int32_t waves;
+    int32_t stages;        // tile buffers per wave (kDec2)
     int32_t rows_per_wg;   // rows handled by one workgroup (row chunk)
     int32_t row_chunks;    // workgroups per (sequence, kv head, split) along rows
     int32_t split_pages;   // pages per workgroup
@@ -61,9 +62,10 @@ struct Plan {
     size_t counter_bytes;  // fused-combine counters
 };
 
-// Default configuration (wgs_per_cu etc.) of the decode (verify = false) or
-// verify unit; used when cfg is NULL and no tuned entry matches.
-q8k4v_config default_config(bool verify);
+// Default configuration for a query block of `rows` rows per kv head (the
+// automatic kernel with its launch-shape defaults); used when cfg is NULL and
+// no tuned entry matches.
+q8k4v_config default_config(int32_t rows);
 
 // Resolve config + shape into a plan; returns Q8K4V_OK or an error.
 int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg, Plan* plan);

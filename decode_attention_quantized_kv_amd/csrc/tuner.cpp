@@ -150,14 +150,15 @@ struct Arena {
 std::string cfg_json(const q8k4v_config& c) {
     char b[256];
     std::snprintf(b, sizeof b,
-                  "{\"variant\":%d,\"waves_per_wg\":%d,\"wgs_per_cu\":%d,\"split_pages\":%d,\"fused_combine\":%d}",
-                  c.variant, c.waves_per_wg, c.wgs_per_cu, c.split_pages, c.fused_combine);
+                  "{\"variant\":%d,\"waves_per_wg\":%d,\"wgs_per_cu\":%d,\"split_pages\":%d,\"fused_combine\":%d,"
+                  "\"stages\":%d}",
+                  c.variant, c.waves_per_wg, c.wgs_per_cu, c.split_pages, c.fused_combine, c.stages);
     return b;
 }
 
 bool same_cfg(const q8k4v_config& a, const q8k4v_config& b) {
     return a.variant == b.variant && a.waves_per_wg == b.waves_per_wg && a.wgs_per_cu == b.wgs_per_cu &&
-           a.split_pages == b.split_pages && a.fused_combine == b.fused_combine;
+           a.split_pages == b.split_pages && a.fused_combine == b.fused_combine && a.stages == b.stages;
 }
 
 std::string fmt(double x) {
@@ -175,6 +176,7 @@ class Tuner {
 
   private:
     bool expired() const { return Clock::now() >= deadline_; }
+    int rows_of(int unit) const { return (unit ? w_ : 1) * g_; }
     int32_t setup(std::string* why);
     int32_t launch(const q8k4v_config* cfg, const Shape& s, int copy, int set, float* out, const void* q);
     int32_t time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us);
@@ -240,11 +242,12 @@ int32_t Tuner::setup(std::string* why) {
     for (int unit = 0; unit < 2; ++unit)
         for (int wgs : {1, 2, 3, 4, 5, 6, 8, 12})
             for (int waves : {1, 2, 4})
-                for (int variant : {0, 1, 2, 3}) {
-                    q8k4v_config c = default_config(unit == 1);
+                for (int variant : {0, 1, 2, 3, 4}) {
+                    q8k4v_config c = default_config(rows_of(unit));
                     c.wgs_per_cu = wgs;
                     c.waves_per_wg = waves;
                     c.variant = variant;
+                    c.stages = 0;
                     c.fused_combine = 1;
                     const int nd = unit ? w_ : 1;
                     ws_bytes_ = std::max(ws_bytes_, q8k4v_workspace_bytes(1, hq_, h_, d_, ctx_l + w_, nd, &c));
@@ -458,9 +461,9 @@ void Tuner::measure(int unit, Cand* c) {
 }
 
 void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, bool* qualified) {
-    const int rows = (unit ? w_ : 1) * g_;
-    const bool dense = !(rows == 1 || rows == 2 || rows == 4 || rows == 8);
-    const q8k4v_config dflt = default_config(unit == 1);
+    const int rows = rows_of(unit);
+    const bool paged16 = rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16;
+    const q8k4v_config dflt = default_config(rows);
     *chosen = dflt;
     *qualified = false;
 
@@ -510,28 +513,46 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
         cands->push_back(x);
         if (x.verdict == "admitted" && x.cost < (*cands)[best_i].cost) best_i = cands->size() - 1;
     };
-    // structural variants: which kernel runs the unit
+    // structural variants: which kernel runs the unit (each with its own
+    // launch-shape defaults)
     std::vector<int> variants;
-    if (dense) variants = {3};
-    else if (rows <= 2) variants = {1};
-    else variants = {2, 1};
+    if (paged16) {
+        if (rows == 4 || rows == 8) variants.push_back(2);
+        if (rows <= 8) variants.push_back(1);
+    }
+    variants.push_back(3);
     for (int v : variants) {
         q8k4v_config c = dflt;
         c.variant = v;
+        c.wgs_per_cu = c.waves_per_wg = c.stages = 0;
         consider(c, "structural");
     }
     // refinement of the launch shape around the best structural choice
-    const int base_variant = (*cands)[best_i].cfg.variant;
-    for (int fused : {0, 1})
-        for (int waves : {2, 4, 1})
-            for (int wgs : {5, 4, 6, 3, 8, 2, 12, 1}) {
-                q8k4v_config c = dflt;
-                c.variant = base_variant;
-                c.waves_per_wg = waves;
-                c.wgs_per_cu = wgs;
-                c.fused_combine = fused;
-                consider(c, "refine");
-            }
+    const q8k4v_config base = (*cands)[best_i].cfg;
+    const bool base_paged = base.variant == 4 || (base.variant == 0 && paged16);
+    for (int fused : {0, 1}) {
+        if (base_paged) {
+            for (int stages : {3, 2})
+                for (int waves : {4, 2})
+                    for (int wgs : {2, 1, 3, 4, 6}) {
+                        q8k4v_config c = base;
+                        c.waves_per_wg = waves;
+                        c.wgs_per_cu = wgs;
+                        c.stages = stages;
+                        c.fused_combine = fused;
+                        consider(c, "refine");
+                    }
+        } else {
+            for (int waves : {2, 4, 1})
+                for (int wgs : {5, 4, 6, 3, 8, 2, 12, 1}) {
+                    q8k4v_config c = base;
+                    c.waves_per_wg = waves;
+                    c.wgs_per_cu = wgs;
+                    c.fused_combine = fused;
+                    consider(c, "refine");
+                }
+        }
+    }
     const Cand& b = (*cands)[best_i];
     *chosen = b.cfg;
     *qualified = b.verdict == "admitted";
@@ -539,9 +560,11 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
 
 int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     const auto t0 = Clock::now();
-    out_table[0] = default_config(false);
-    out_table[1] = default_config(true);
     std::string why;
+    g_ = req_.num_q_heads / req_.num_kv_heads;
+    w_ = req_.n_draft;
+    out_table[0] = default_config(rows_of(0));
+    out_table[1] = default_config(rows_of(1));
     int32_t rc = setup(&why);
     std::vector<Cand> cands[2];
     q8k4v_config chosen[2] = {out_table[0], out_table[1]};
@@ -555,7 +578,7 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
         out_table[unit] = chosen[unit];
         out_table[unit].qualified = qual[unit] ? 1 : 0;
         if (!qual[unit]) {
-            out_table[unit] = default_config(unit == 1);
+            out_table[unit] = default_config(rows_of(unit));
             out_table[unit].qualified = 0;
         }
     }

@@ -91,8 +91,10 @@ def test_workspace_size_follows_the_plan(lib):
     small = q8.workspace_bytes(1, 32, 8, 128, 64)
     big = q8.workspace_bytes(1, 32, 8, 128, 65536)
     assert big > 0 and big >= small
-    cfg = q8.make_config(split_pages=4096)
+    cfg = q8.make_config(split_pages=4096, variant=2)
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, cfg) == 0     # one split: direct write
+    # variant 4 keeps at most 64 pages per wave: 4096 pages need splits
+    assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(split_pages=4096, variant=4)) > 0
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(waves_per_wg=3)) == 0  # invalid config
     assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(variant=2)) == 0  # 1 row: no block MFMA
 

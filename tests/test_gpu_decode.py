@@ -16,8 +16,10 @@ CONFIGS = [None,
            dict(variant=1, waves_per_wg=2, tile_pages=4), dict(variant=1, waves_per_wg=1, tile_pages=4),
            dict(variant=1, waves_per_wg=1, tile_pages=1), dict(variant=1, fused_combine=0),
            dict(variant=2, waves_per_wg=1), dict(variant=2, waves_per_wg=4), dict(variant=2, fused_combine=0),
-           dict(split_pages=1), dict(split_pages=3, waves_per_wg=1), dict(wgs_per_cu=8),
-           dict(wgs_per_cu=1, fused_combine=0)]
+           dict(split_pages=1), dict(split_pages=3, waves_per_wg=2), dict(wgs_per_cu=8),
+           dict(wgs_per_cu=1, fused_combine=0),
+           dict(variant=4, stages=2), dict(variant=4, waves_per_wg=2, stages=3), dict(variant=4, fused_combine=1),
+           dict(variant=4, split_pages=5, waves_per_wg=2, stages=2), dict(variant=3), dict(variant=3, fused_combine=1)]
 
 
 def _cfg(d):
