@@ -47,9 +47,19 @@ def _source_hash() -> str:
     return h.hexdigest()[:12]
 
 
+# MFMA accumulators in ordinary VGPRs (gfx950's unified register file): the
+# online-softmax rescale then multiplies them in place instead of copying
+# them out of and back into accumulation registers.
+PER_SOURCE = {
+    "attn_dec2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str, build_id: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, f'-DQ8K4V_BUILD_ID="{build_id}"', "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_SOURCE.get(src, []), f'-DQ8K4V_BUILD_ID="{build_id}"', "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

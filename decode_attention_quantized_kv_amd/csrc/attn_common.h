@@ -196,19 +196,23 @@ Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
     fused_tail<D, RW>(p, w, r0);
 }
 
-// Separate combine kernel: one 256-thread workgroup per (b, kh, row).  All
-// split records of the row are loaded at once: first the per-split (max,
-// sum) pairs, reduced to the row's reference and weights in LDS; then the
-// partial outputs as float4 columns, each thread summing a strided subset of
-// the splits, and a tree over the subsets.
+// Separate combine kernel: one 256-thread workgroup per (b, kh, row).
+// Thread (split group sg, float4 column qc) loads the records of splits sg,
+// sg + SG, ... in chunks of 8 -- maxima, sums and its output column, all
+// loads of a chunk issued together -- and merges them online; the SG group
+// states are then merged through LDS.  The partials come from the previous
+// kernel on the stream, so plain loads see them.  Records are loaded for
+// every split of the launch (all in bounds) and those past the sequence's
+// last split are masked afterwards, so the loads do not wait for seq_lens.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     constexpr int NQ = D / 4;                 // float4 columns of a row
     constexpr int SG = 256 / NQ;              // split groups
-    __shared__ float s_w[kCombineMaxSplits];
-    __shared__ float s_red[8];
-    __shared__ f32x4 s_acc[SG][NQ];
+    constexpr int CH = 8;                     // splits per load batch
+    __shared__ float s_m[SG], s_l[SG];
+    __shared__ f32x4 s_o[SG][NQ];
     const int t = threadIdx.x;
+    const int qc = t % NQ, sg = t / NQ;
     const int r = blockIdx.x % p.R;
     const int kh = (blockIdx.x / p.R) % p.H;
     const int b = blockIdx.x / (p.R * p.H);
@@ -217,44 +221,63 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     const int n_eff = min(p.n_splits, (npages + p.split_pages - 1) / p.split_pages);
     const size_t rs = (size_t)p.R * partial_stride<D>();
     const float* base = p.partials + ((size_t)b * p.H + kh) * p.n_splits * rs + (size_t)r * partial_stride<D>();
-    // phase 1: reference max and weights
-    float M = kNegInf;
-    for (int s = t; s < n_eff; s += 256) {
-        const float m = load_coherent(base + s * rs);
-        s_w[s] = m;
-        M = fmaxf(M, m);
+    float M = kNegInf, Ls = 0.0f;
+    f32x4 O = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = sg; s0 < p.n_splits; s0 += SG * CH) {
+        float m[CH], l[CH];
+        f32x4 o[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int s = s0 + c * SG;
+            if (s < p.n_splits) {
+                const float* rec = base + (size_t)s * rs;
+                m[c] = rec[0];
+                l[c] = rec[1];
+                o[c] = *((const f32x4*)(rec + 4) + qc);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (s0 + c * SG >= n_eff) {
+                m[c] = kNegInf;
+                l[c] = 0.0f;
+                o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        float Mn = M;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, m[c]);
+        if (Mn != kNegInf) {
+            const float a = exp2_fast(M - Mn);       // M = -inf gives 0
+            O *= a;
+            Ls *= a;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const float wgt = exp2_fast(m[c] - Mn);
+                O += o[c] * wgt;
+                Ls += l[c] * wgt;
+            }
+            M = Mn;
+        }
     }
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if ((t & 63) == 0) s_red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float ref = (M == kNegInf) ? 0.0f : M;
-    float Ls = 0.0f;
-    for (int s = t; s < n_eff; s += 256) {
-        const float wgt = exp2_fast(s_w[s] - ref);
-        s_w[s] = wgt;
-        Ls += load_coherent(base + s * rs + 1) * wgt;
+    if (qc == 0) {
+        s_m[sg] = M;
+        s_l[sg] = Ls;
     }
-    for (int o = 1; o < 64; o <<= 1) Ls += __shfl_xor(Ls, o);
-    __syncthreads();
-    if ((t & 63) == 0) s_red[4 + (t >> 6)] = Ls;
-    __syncthreads();
-    const float Lt = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-    // phase 2: weighted sum of the partial outputs
-    const int qc = t % NQ, sg = t / NQ;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4* col = (const f32x4*)(base + 4) + qc;
-#pragma unroll 8
-    for (int s = sg; s < n_eff; s += SG) {
-        const f32x4 v = *(col + s * (rs / 4));
-        acc += v * s_w[s];
-    }
-    s_acc[sg][qc] = acc;
+    s_o[sg][qc] = O;
     __syncthreads();
     if (t < NQ) {
-        f32x4 sum = s_acc[0][t];
+        float Mg = kNegInf;
 #pragma unroll
-        for (int g = 1; g < SG; ++g) sum += s_acc[g][t];
+        for (int g = 0; g < SG; ++g) Mg = fmaxf(Mg, s_m[g]);
+        const float ref = (Mg == kNegInf) ? 0.0f : Mg;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        float Lt = 0.0f;
+#pragma unroll
+        for (int g = 0; g < SG; ++g) {
+            const float wgt = exp2_fast(s_m[g] - ref);
+            sum += s_o[g][t] * wgt;
+            Lt += s_l[g] * wgt;
+        }
         const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
         f32x4* dst = (f32x4*)(p.out + out_index(p, b, kh, r, D)) + t;
         *dst = sum * inv;

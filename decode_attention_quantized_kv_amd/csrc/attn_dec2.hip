@@ -153,14 +153,12 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
             if (lane < 2 * NG) lds_dma16(p.v_scales + blk * 16 * NG, lane * 16, base + OFF_VS + u * VSB);
         }
     };
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nt) issue(s, s);
-
     // ---- query row (n mod R) as the B operand: 15-bit fixed point
     // Q = rne(q * 2^(14-e)) (2^(e-1) <= max|q_row| < 2^e), int8 halves
     // hi = (Q + 128) >> 8, lo = Q - 256 hi; lane (n, q) holds dims
     // 64 ks + 16 q .. +15 of every k-step ks
+    // (the query loads go out with the page-id load, before the first
+    // copies: the compiler's wait for them then covers no copy)
     u32x4 qhi[KS], qlo[KS];
     float coef;
     int lim;
@@ -194,25 +192,29 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(x[ks][i]));
         mx = xgroups_max(mx);
+        // the first tiles' copies go out now; the conversion below overlaps them
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nt) issue(s, s);
         int e = 0;
         if (mx > 0.0f) (void)frexpf(mx, &e);
         e = min(max(e, -110), 110);
         const float sc = ldexpf(1.0f, 14 - e);
+        // U = Q + 128 by one fma against 1.5 * 2^23 + 128: |Q| <= 2^14, so the
+        // sum's low 16 bits are U (round-half-even like rintf); then
+        // hi byte = U >> 8, lo byte = (U & 0xFF) - 128 = (U ^ 0x80) & 0xFF
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                uint32_t h4 = 0, l4 = 0;
+                uint32_t u[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int Q = (int)rintf(x[ks][4 * c + t] * sc);
-                    const int hi = (Q + 128) >> 8;
-                    h4 |= (uint32_t)(hi & 0xFF) << (8 * t);
-                    l4 |= (uint32_t)((Q - 256 * hi) & 0xFF) << (8 * t);
-                }
-                hw[c] = h4;
-                lw[c] = l4;
+                for (int t = 0; t < 4; ++t) u[t] = fbits(__builtin_fmaf(x[ks][4 * c + t], sc, 12583040.0f));
+                const uint32_t u01 = __builtin_amdgcn_perm(u[1], u[0], 0x05040100u);   // U0 | U1 << 16
+                const uint32_t u23 = __builtin_amdgcn_perm(u[3], u[2], 0x05040100u);
+                hw[c] = __builtin_amdgcn_perm(u23, u01, 0x07050301u);                 // byte 1 of U0..U3
+                lw[c] = __builtin_amdgcn_perm(u23, u01, 0x06040200u) ^ 0x80808080u;   // byte 0 of U0..U3
             }
             qhi[ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
             qlo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
