@@ -76,7 +76,7 @@ bool dec2_rows(int32_t rows) { return rows == 1 || rows == 2 || rows == 4 || row
 // launch shape defaults per kernel
 void kernel_defaults(int32_t kernel, q8k4v_config* c) {
     switch (kernel) {
-        case kDec2: c->wgs_per_cu = 2; c->waves_per_wg = 4; c->stages = 3; c->tile_pages = 2; break;
+        case kDec2: c->wgs_per_cu = 1; c->waves_per_wg = 4; c->stages = 2; c->tile_pages = 2; break;
         case kMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 2; break;
         case kBlockMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
         default: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
@@ -171,9 +171,12 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = kd.wgs_per_cu;
     if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = kd.waves_per_wg;
     if (cfg.stages <= 0) cfg.stages = kd.stages;
-    if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4)
+    if (kernel == kDec2) {
+        if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
+            return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");
+    } else if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4) {
         return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
-    if (kernel == kDec2 && cfg.waves_per_wg == 1) return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2 or 4 waves");
+    }
     if (kernel == kDec2 && cfg.stages != 2 && cfg.stages != 3) return fail(Q8K4V_EINVAL, "attention: stages must be 2 or 3");
     // tiles: the MFMA kernels fix their tile length
     if (kernel == kBlockMfma) cfg.tile_pages = 4;

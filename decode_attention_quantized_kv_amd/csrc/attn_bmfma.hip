@@ -360,7 +360,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bmfma_kernel(const AttnParams
         for (int h = 0; h < DH; ++h)
 #pragma unroll
             for (int m = 0; m < 4; ++m) s_o[(wave * R + 4 * s + m) * D + 64 * h + vdim] = acc[s][h][m];
-    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o);
+    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, &s_stage[0][0], (int)sizeof(s_stage));
 }
 
 template <int D, int RB4, int WAVES, bool QBF16>

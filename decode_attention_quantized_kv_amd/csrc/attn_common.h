@@ -83,54 +83,98 @@ Q8K4V_DEV void write_zero_rows(const AttnParams& p, const WorkItem& w, int r0, i
 }
 
 // Log-sum-exp merge of the n_eff split partials of (b, kh) for rows
-// [r0, r0 + NR), by the threads of one workgroup: one wave per row gathers
-// the split maxima and sums in parallel, then every thread streams the
-// partial outputs of its (row, dimension) elements with independent loads.
+// [r0, r0 + NR), by the threads of the last workgroup to finish.  The split
+// records were written with write-through stores by workgroups on any XCD;
+// an agent-scope acquire (which invalidates this XCD's L2) lets plain,
+// vectorised loads see them.  Thread t takes (row, float4 column) pairs and
+// a split group, loads the records of its splits in batches of CH with all
+// loads of a batch in flight, merges them online, and the split groups are
+// merged through LDS.
 constexpr int kCombineMaxSplits = 1024;
 
 template <int D, int NR>
-Q8K4V_DEV void combine_splits(const AttnParams& p, int b, int kh, int r0, int n_eff) {
-    __shared__ float s_ref[NR], s_inv[NR];
+Q8K4V_DEV void combine_splits(const AttnParams& p, int b, int kh, int r0, int n_eff, void* scratch,
+                              int scratch_bytes) {
+    constexpr int NQ = D / 4;
+    constexpr int NP = NR * NQ;               // (row, column) pairs
+    constexpr int CH = 16;
+    constexpr int REC = 24;                   // LDS bytes per pair and group: m, l, o
+    const int nt = blockDim.x;
+    const int sg_n = max(1, min(nt / NP, scratch_bytes / (REC * NP)));   // split groups
+    const int chunk = min(NP, max(1, scratch_bytes / (REC * sg_n)));    // pairs per pass
+    float* s_m = (float*)scratch;             // [sg_n][chunk]
+    float* s_l = s_m + sg_n * chunk;
+    f32x4* s_o = (f32x4*)(s_l + sg_n * chunk + ((4 - (2 * sg_n * chunk) % 4) % 4));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const size_t rs = (size_t)p.R * partial_stride<D>();
     const float* base = p.partials + ((size_t)b * p.H + kh) * p.n_splits * rs;
-    const int nt = blockDim.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = nt >> 6;
-    for (int rl = wave; rl < NR; rl += nw) {
-        const int r = r0 + rl;
-        float M = kNegInf;
-        if (r < p.R)
-            for (int s = lane; s < n_eff; s += 64) M = fmaxf(M, load_coherent(base + s * rs + (size_t)r * partial_stride<D>()));
-        for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-        const float ref = (M == kNegInf) ? 0.0f : M;
-        float Ls = 0.0f;
-        if (r < p.R)
-            for (int s = lane; s < n_eff; s += 64) {
-                const float* rec = base + s * rs + (size_t)r * partial_stride<D>();
-                Ls += load_coherent(rec + 1) * exp2_fast(load_coherent(rec) - ref);
+    for (int pc0 = 0; pc0 < NP; pc0 += chunk) {
+        const int npc = min(chunk, NP - pc0);
+        for (int t = threadIdx.x; t < npc * sg_n; t += nt) {
+            const int pl = t % npc, sg = t / npc;
+            const int pr = pc0 + pl;
+            const int rl = pr / NQ, qc = pr % NQ;
+            const int r = min(r0 + rl, p.R - 1);
+            const float* rbase = base + (size_t)r * partial_stride<D>();
+            float M = kNegInf, Ls = 0.0f;
+            f32x4 O = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s0 = sg; s0 < n_eff; s0 += sg_n * CH) {
+                float m[CH], l[CH];
+                f32x4 o[CH];
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int sp = s0 + c * sg_n;
+                    if (sp < n_eff) {
+                        const float* rec = rbase + (size_t)sp * rs;
+                        m[c] = rec[0];
+                        l[c] = rec[1];
+                        o[c] = *((const f32x4*)(rec + 4) + qc);
+                    } else {
+                        m[c] = kNegInf;
+                        l[c] = 0.0f;
+                        o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+                }
+                float Mn = M;
+#pragma unroll
+                for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, m[c]);
+                if (Mn != kNegInf) {
+                    const float a = exp2_fast(M - Mn);
+                    O *= a;
+                    Ls *= a;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const float wgt = exp2_fast(m[c] - Mn);
+                        O += o[c] * wgt;
+                        Ls += l[c] * wgt;
+                    }
+                    M = Mn;
+                }
             }
-        for (int o = 1; o < 64; o <<= 1) Ls += __shfl_xor(Ls, o);
-        if (lane == 0) {
-            s_ref[rl] = ref;
-            s_inv[rl] = (Ls > 0.0f) ? 1.0f / Ls : 0.0f;
+            s_m[sg * chunk + pl] = M;
+            s_l[sg * chunk + pl] = Ls;
+            s_o[sg * chunk + pl] = O;
         }
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < NR * D; e += nt) {
-        const int rl = e / D, d = e % D;
-        const int r = r0 + rl;
-        if (r >= p.R) continue;
-        const float ref = s_ref[rl];
-        const float* rec = base + (size_t)r * partial_stride<D>();
-        float O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
-        int s = 0;
-        for (; s + 4 <= n_eff; s += 4) {
-            O0 += load_coherent(rec + (s + 0) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 0) * rs) - ref);
-            O1 += load_coherent(rec + (s + 1) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 1) * rs) - ref);
-            O2 += load_coherent(rec + (s + 2) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 2) * rs) - ref);
-            O3 += load_coherent(rec + (s + 3) * rs + 4 + d) * exp2_fast(load_coherent(rec + (s + 3) * rs) - ref);
+        __syncthreads();
+        for (int pl = threadIdx.x; pl < npc; pl += nt) {
+            const int pr = pc0 + pl;
+            const int rl = pr / NQ, qc = pr % NQ;
+            const int r = r0 + rl;
+            if (r >= p.R) continue;
+            float Mg = kNegInf;
+            for (int g = 0; g < sg_n; ++g) Mg = fmaxf(Mg, s_m[g * chunk + pl]);
+            const float ref = (Mg == kNegInf) ? 0.0f : Mg;
+            f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+            float Lt = 0.0f;
+            for (int g = 0; g < sg_n; ++g) {
+                const float wgt = exp2_fast(s_m[g * chunk + pl] - ref);
+                sum += s_o[g * chunk + pl] * wgt;
+                Lt += s_l[g * chunk + pl] * wgt;
+            }
+            const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
+            *((f32x4*)(p.out + out_index(p, b, kh, r, D)) + qc) = sum * inv;
         }
-        for (; s < n_eff; ++s) O0 += load_coherent(rec + s * rs + 4 + d) * exp2_fast(load_coherent(rec + s * rs) - ref);
-        p.out[out_index(p, b, kh, r, D) + d] = ((O0 + O1) + (O2 + O3)) * s_inv[rl];
+        __syncthreads();
     }
 }
 
@@ -152,7 +196,7 @@ Q8K4V_DEV void emit_element(const AttnParams& p, const WorkItem& w, int r, int d
 // With the fused combine, the last workgroup of (b, kh, row chunk) to finish
 // merges all splits.  Called by every thread after its emit_element calls.
 template <int D, int RW>
-Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0) {
+Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0, void* scratch, int scratch_bytes) {
     if (p.direct || !p.fused) return;
     __shared__ int s_last;
     const int n_eff = (w.npages + p.split_pages - 1) / p.split_pages;
@@ -167,14 +211,17 @@ Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0) {
     }
     __syncthreads();
     if (!s_last) return;
-    combine_splits<D, RW>(p, w.b, w.kh, r0, n_eff);
+    combine_splits<D, RW>(p, w.b, w.kh, r0, n_eff, scratch, scratch_bytes);
 }
 
 // Merge the waves of a workgroup (each wave left its running max m, sum l
 // and unnormalised output o in LDS), then emit the rows.
+// `scratch` (scratch_bytes of LDS, 16-byte aligned, s_o may lie in it) is
+// free for the fused combine once the rows are emitted.
 template <int D, int RW, int WAVES>
 Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
-                                const float (*s_ml)[RW][2], const float* s_o /* [WAVES][RW][D] */) {
+                                const float (*s_ml)[RW][2], const float* s_o /* [WAVES][RW][D] */,
+                                void* scratch, int scratch_bytes) {
     __syncthreads();
     for (int e = threadIdx.x; e < RW * D; e += 64 * WAVES) {
         const int rl = e / D, d = e % D;
@@ -193,7 +240,8 @@ Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
         }
         emit_element<D>(p, w, r, d, M, Ls, O);
     }
-    fused_tail<D, RW>(p, w, r0);
+    if (p.fused && !p.direct) __syncthreads();   // s_o is read above; the merge reuses it
+    fused_tail<D, RW>(p, w, r0, scratch, scratch_bytes);
 }
 
 // Separate combine kernel: one 256-thread workgroup per (b, kh, row).

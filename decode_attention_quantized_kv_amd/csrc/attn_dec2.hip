@@ -385,7 +385,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
                 s_o[(wave * R + idx % R) * D + 16 * dt + n16] = acc[dt][i];
         }
     }
-    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o);
+    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, &s_stage[0][0][0], (int)sizeof(s_stage));
 }
 
 template <int D, int R, int WAVES, int STAGES, bool QBF16>
@@ -404,6 +404,8 @@ LaunchFn pick_shape(int waves, int stages) {
     if (waves == 2 && stages == 3) return &launch_t<D, R, 2, 3, QBF16>;
     if (waves == 4 && stages == 2) return &launch_t<D, R, 4, 2, QBF16>;
     if (waves == 4 && stages == 3) return &launch_t<D, R, 4, 3, QBF16>;
+    if (waves == 8 && stages == 2) return &launch_t<D, R, 8, 2, QBF16>;
+    if (waves == 8 && stages == 3) return &launch_t<D, R, 8, 3, QBF16>;
     return nullptr;
 }
 

@@ -363,7 +363,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_mfma_kernel(const AttnParams 
         for (int u = 0; u < WAVES; ++u) Ls += s_ml[u][rl][1] * exp2_fast(s_ml[u][rl][0] - ref);
         emit_element<D>(p, w, r, d, M, Ls, s_o[rl * D + d]);
     }
-    fused_tail<D, RW>(p, w, r0);
+    if (p.fused && !p.direct) __syncthreads();   // s_merge is read above; the merge reuses the ring
+    fused_tail<D, RW>(p, w, r0, &s_stage[0][0], (int)sizeof(s_stage));
 }
 
 template <int D, int RB, int WAVES, bool QBF16>

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_valu_kernel(const AttnParams 
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int e = 0; e < DPL; ++e) s_o[(wave * R + r) * D + DPL * lane + e] = acc[r][e];
-    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o);
+    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, &s_stage[0][0], (int)sizeof(s_stage));
 }
 
 template <int D, int R, int WAVES, int TP, bool QBF16>

@@ -533,8 +533,9 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
     for (int fused : {0, 1}) {
         if (base_paged) {
             for (int stages : {3, 2})
-                for (int waves : {4, 2})
+                for (int waves : {4, 8, 2})
                     for (int wgs : {2, 1, 3, 4, 6}) {
+                        if (waves == 8 && wgs > 1) continue;   // one 8-wave workgroup fills a CU's LDS
                         q8k4v_config c = base;
                         c.waves_per_wg = waves;
                         c.wgs_per_cu = wgs;
