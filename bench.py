@@ -229,8 +229,8 @@ def main() -> int:
 # the summary is used only while these files are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    False: ["attn_bmfma.hip", "attn_valu.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp"],
-    True: ["attn_mfma.hip", "attn_bmfma.hip", "attn_valu.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp"],
+    False: ["attn_paged.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp"],
+    True: ["attn_paged.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp"],
 }
 
 

@@ -25,7 +25,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libq8k4v.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "q8k4v")
 
-SOURCES = ["abi.cpp", "append.hip", "attn_valu.hip", "attn_bmfma.hip", "attn_mfma.hip", "attn_dec2.hip", "tuner.cpp"]
+SOURCES = ["abi.cpp", "append.hip", "attn_valu.hip", "attn_bmfma.hip", "attn_mfma.hip", "attn_paged.hip", "tuner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
@@ -51,7 +51,7 @@ def _source_hash() -> str:
 # online-softmax rescale then multiplies them in place instead of copying
 # them out of and back into accumulation registers.
 PER_SOURCE = {
-    "attn_dec2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 

@@ -22,6 +22,7 @@ int32_t launch_valu(const AttnParams& kp, const Plan& plan, int head_dim, bool q
 int32_t launch_bmfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_mfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
+int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
 
 namespace {
@@ -77,13 +78,14 @@ bool dec2_rows(int32_t rows) { return rows == 1 || rows == 2 || rows == 4 || row
 void kernel_defaults(int32_t kernel, q8k4v_config* c) {
     switch (kernel) {
         case kDec2: c->wgs_per_cu = 1; c->waves_per_wg = 4; c->stages = 2; c->tile_pages = 2; break;
+        case kRows: c->wgs_per_cu = 1; c->waves_per_wg = 4; c->stages = 2; c->tile_pages = 2; break;
         case kMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 2; break;
         case kBlockMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
         default: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
     }
 }
 
-int32_t auto_kernel(int32_t rows) { return dec2_rows(rows) ? kDec2 : kMfma; }
+int32_t auto_kernel(int32_t rows) { return dec2_rows(rows) ? kDec2 : kRows; }
 }  // namespace
 
 q8k4v_config default_config(int32_t rows) {
@@ -163,7 +165,8 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
             if (!dec2_rows(rows)) return fail(Q8K4V_EINVAL, "attention: variant 4 needs 1, 2, 4, 8 or 16 rows per kv head");
             kernel = kDec2;
             break;
-        default: return fail(Q8K4V_EINVAL, "attention: variant must be 0..4");
+        case 5: kernel = kRows; break;
+        default: return fail(Q8K4V_EINVAL, "attention: variant must be 0..5");
     }
     q8k4v_config kd;
     std::memset(&kd, 0, sizeof(kd));
@@ -174,17 +177,21 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     if (kernel == kDec2) {
         if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
             return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");
+    } else if (kernel == kRows) {
+        if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4)
+            return fail(Q8K4V_EINVAL, "attention: variant 5 needs 2 or 4 waves per workgroup");
     } else if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4) {
         return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
     }
-    if (kernel == kDec2 && cfg.stages != 2 && cfg.stages != 3) return fail(Q8K4V_EINVAL, "attention: stages must be 2 or 3");
+    if ((kernel == kDec2 || kernel == kRows) && cfg.stages != 2 && cfg.stages != 3)
+        return fail(Q8K4V_EINVAL, "attention: stages must be 2 or 3");
     // tiles: the MFMA kernels fix their tile length
     if (kernel == kBlockMfma) cfg.tile_pages = 4;
-    else if (kernel == kMfma || kernel == kDec2) cfg.tile_pages = 2;
+    else if (kernel == kMfma || kernel == kDec2 || kernel == kRows) cfg.tile_pages = 2;
     else if (cfg.tile_pages <= 0) cfg.tile_pages = kd.tile_pages;
     if (cfg.tile_pages != 1 && cfg.tile_pages != 2 && cfg.tile_pages != 4)
         return fail(Q8K4V_EINVAL, "attention: tile_pages must be 1, 2 or 4");
-    const bool dense = kernel == kMfma;
+    const bool dense = kernel == kMfma || kernel == kRows;
 
     plan->rows = rows;
     plan->kernel = kernel;
@@ -192,7 +199,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     plan->tile_pages = cfg.tile_pages;
     plan->waves = cfg.waves_per_wg;
     plan->stages = cfg.stages;
-    plan->rows_per_wg = (kernel == kMfma) ? (rows > 16 ? 32 : 16) : rows;
+    plan->rows_per_wg = (kernel == kMfma || kernel == kRows) ? (rows > 16 ? 32 : 16) : rows;
     plan->row_chunks = (rows + plan->rows_per_wg - 1) / plan->rows_per_wg;
     const int32_t max_np = std::max(1, (a.max_seq_len + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE);
     const int32_t unit = cfg.tile_pages * cfg.waves_per_wg;      // pages per workgroup step
@@ -206,7 +213,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);
     }
     sp = std::max(sp, unit);
-    if (kernel == kDec2) sp = std::min(sp, 64 * cfg.waves_per_wg);   // <= 64 pages per wave
+    if (kernel == kDec2 || kernel == kRows) sp = std::min(sp, 64 * cfg.waves_per_wg);   // <= 64 pages per wave
     plan->split_pages = sp;
     plan->n_splits = (max_np + sp - 1) / sp;
     if (plan->n_splits > kCombineMaxSplits) {   // the combine holds one weight per split in LDS
@@ -214,8 +221,8 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         plan->split_pages = sp;
         plan->n_splits = (max_np + sp - 1) / sp;
     }
-    if (kernel == kDec2 && plan->split_pages > 64 * cfg.waves_per_wg)
-        return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long for variant 4 (more than 1024 splits)");
+    if ((kernel == kDec2 || kernel == kRows) && plan->split_pages > 64 * cfg.waves_per_wg)
+        return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long for variants 4 and 5 (more than 1024 splits)");
     plan->fused_combine = (plan->n_splits > 1 && cfg.fused_combine) ? 1 : 0;
     const size_t rec = (size_t)(a.cache->head_dim + 4) * sizeof(float);
     plan->partial_bytes = plan->n_splits > 1 ? (size_t)a.n_seqs * H * plan->n_splits * rows * rec : 0;
@@ -264,6 +271,7 @@ int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, s
         case kVector: rc = launch_valu(kp, plan, c.head_dim, bf, stream); break;
         case kBlockMfma: rc = launch_bmfma(kp, plan, c.head_dim, bf, stream); break;
         case kDec2: rc = launch_dec2(kp, plan, c.head_dim, bf, stream); break;
+        case kRows: rc = launch_rows(kp, plan, c.head_dim, bf, stream); break;
         default: rc = launch_mfma(kp, plan, c.head_dim, bf, stream); break;
     }
     if (rc != Q8K4V_OK) return rc;

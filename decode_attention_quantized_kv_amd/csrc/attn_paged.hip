@@ -388,6 +388,378 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
     finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, &s_stage[0][0][0], (int)sizeof(s_stage));
 }
 
+// ---------------------------------------------------------------------------
+// Row-block variant for query blocks of up to 32 rows per workgroup (verify:
+// drafts x group), rows padded to RB blocks of 16.  The tile ring, page ids
+// and the query's fixed-point form are those of attn_dec2_kernel; here the
+// MFMA columns are 16 distinct query rows per block (no replication):
+//  * S^T = K Q^T per page and row block on v_mfma_i32_16x16x64_i8: lane
+//    (n, q) gets row 16 rb + n's scores of tokens 4q .. 4q+3;
+//  * A operand per (row block, value group): the lane's probabilities of
+//    its 8 tokens, rounded to fp16, times the tokens' group scales (packed
+//    fp16 multiply; products of p <= 1 and an fp16 scale cannot overflow);
+//  * O tile dt (value group dt/2) on v_mfma_f32_16x16x32_f16 with the exact
+//    fp16 value codes: lane (n, q) holds rows 16 rb + 4q + i, dim 16 dt + n.
+// The waves' outputs are merged in wave order through one LDS buffer.
+// ---------------------------------------------------------------------------
+template <int D, int RB, int WAVES, int STAGES, bool QBF16>
+__global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
+    constexpr int TP = 2;
+    constexpr int KB = 16 * D, VB = 8 * D;
+    constexpr int NG = D / 32;
+    constexpr int KSB = 32, VSB = 32 * NG;
+    constexpr int OFF_V = TP * KB, OFF_KS = OFF_V + TP * VB, OFF_VS = OFF_KS + TP * KSB;
+    constexpr int STAGE = OFF_VS + TP * VSB;
+    constexpr int CPR = D / 16;
+    constexpr int KS = D / 64;
+    constexpr int NDT = D / 16;
+    constexpr int KI = KB / 1024;
+    constexpr int IPT = TP * (KI + 3);
+    constexpr int RW = 16 * RB;                // rows per workgroup
+    constexpr int NVW = NG / 2;                // 32-bit words of one token's value scales
+    static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
+    static_assert(RW * D * 4 <= WAVES * STAGES * STAGE, "the merge buffer reuses the tile ring");
+
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES][STAGES][STAGE];
+    __shared__ float s_ml[WAVES][RW][2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    WorkItem w;
+    if (!work_item(p, w)) return;
+    const int r0 = w.rchunk * RW;
+    if (w.pbeg >= w.pend) {
+        if (w.split == 0) write_zero_rows<D>(p, w, r0, RW);
+        return;
+    }
+    const int n16 = lane & 15;
+    const int q4 = lane >> 4;
+    const int kh = w.kh, pend = w.pend;
+    const int ntile_all = (pend - w.pbeg + TP - 1) / TP;
+    const int nt = ntile_all > wave ? (ntile_all - wave + WAVES - 1) / WAVES : 0;   // <= 32 (planner)
+
+    int my_id = 0;
+    {
+        const int pg = w.pbeg + TP * (wave + WAVES * (lane >> 1)) + (lane & 1);
+        if (lane < TP * nt) my_id = p.page_table[(size_t)w.b * p.max_pages + min(pg, pend - 1)];
+    }
+    uint8_t* const stage0 = &s_stage[wave][0][0];
+    const uint32_t lds0 = lds_addr(stage0);
+    uint32_t kdma_off[KI];
+#pragma unroll
+    for (int c = 0; c < KI; ++c) {
+        const int s = 64 * c + lane;
+        const int t = s / CPR, cc = (s % CPR) ^ (t % CPR);
+        kdma_off[c] = (uint32_t)(t * D + 16 * cc);
+    }
+    auto issue = [&](int t, int slot) {
+        const uint32_t base = lds0 + slot * STAGE;
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const int id = __builtin_amdgcn_readlane(my_id, TP * t + u);
+            const size_t blk = (size_t)id * p.H + kh;
+#pragma unroll
+            for (int c = 0; c < KI; ++c) lds_dma16(p.k_codes + blk * KB, kdma_off[c], base + u * KB + c * 1024);
+            if (VB >= 1024) {
+                lds_dma16(p.v_codes + blk * VB, lane * 16, base + OFF_V + u * VB);
+            } else if (lane < VB / 16) {
+                lds_dma16(p.v_codes + blk * VB, lane * 16, base + OFF_V + u * VB);
+            }
+            if (lane < 2) lds_dma16(p.k_scales + blk * 16, lane * 16, base + OFF_KS + u * KSB);
+            if (lane < 2 * NG) lds_dma16(p.v_scales + blk * 16 * NG, lane * 16, base + OFF_VS + u * VSB);
+        }
+    };
+
+    // ---- query rows r0 + 16 rb + n as B operands (15-bit fixed point, int8
+    // halves; rows past R are zero)
+    u32x4 qhi[RB][KS], qlo[RB][KS];
+    float coef[RB];
+    int lim[RB];
+    {
+        float x[RB][KS][16];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = r0 + 16 * rb + n16;
+            const bool ok = r < p.R;
+            const size_t qoff = out_index(p, w.b, kh, ok ? r : 0, D);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int d0 = 64 * ks + 16 * q4;
+                if (QBF16) {
+                    const u32x4* src = (const u32x4*)((const uint16_t*)p.q + qoff + d0);
+                    const u32x4 a = src[0], b = src[1];
+                    const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        x[rb][ks][2 * i] = ok ? bitsf(wd[i] << 16) : 0.0f;
+                        x[rb][ks][2 * i + 1] = ok ? bitsf(wd[i] & 0xFFFF0000u) : 0.0f;
+                    }
+                } else {
+                    const f32x4* src = (const f32x4*)((const float*)p.q + qoff + d0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x4 v = src[i];
+                        x[rb][ks][4 * i] = ok ? v.x : 0.0f;
+                        x[rb][ks][4 * i + 1] = ok ? v.y : 0.0f;
+                        x[rb][ks][4 * i + 2] = ok ? v.z : 0.0f;
+                        x[rb][ks][4 * i + 3] = ok ? v.w : 0.0f;
+                    }
+                }
+            }
+            lim[rb] = ok ? w.L - p.W + 1 + r / p.G : 0;
+        }
+        float mx[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            mx[rb] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx[rb] = fmaxf(mx[rb], fabsf(x[rb][ks][i]));
+            mx[rb] = xgroups_max(mx[rb]);
+        }
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nt) issue(s, s);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            int e = 0;
+            if (mx[rb] > 0.0f) (void)frexpf(mx[rb], &e);
+            e = min(max(e, -110), 110);
+            const float sc = ldexpf(1.0f, 14 - e);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    uint32_t u[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) u[t] = fbits(__builtin_fmaf(x[rb][ks][4 * c + t], sc, 12583040.0f));
+                    const uint32_t u01 = __builtin_amdgcn_perm(u[1], u[0], 0x05040100u);
+                    const uint32_t u23 = __builtin_amdgcn_perm(u[3], u[2], 0x05040100u);
+                    hw[c] = __builtin_amdgcn_perm(u23, u01, 0x07050301u);
+                    lw[c] = __builtin_amdgcn_perm(u23, u01, 0x06040200u) ^ 0x80808080u;
+                }
+                qhi[rb][ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+                qlo[rb][ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+            }
+            coef[rb] = p.scale_log2 * ldexpf(1.0f, e - 14);
+        }
+    }
+    const int lim_min = w.L - p.W + 1;
+
+    float m_run[RB], l_run[RB];
+    f32x4 acc[RB][NDT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = kNegInf;
+        l_run[rb] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[rb][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    for (int t = 0; t < nt; ++t) {
+        const int slot = t % STAGES;
+        if (t + STAGES - 1 < nt) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
+        const int after = min(STAGES - 1, nt - 1 - t);
+        if (STAGES == 3 && after >= 2) wait_vmem<2 * IPT>();
+        else if (after >= 1) wait_vmem<IPT>();
+        else wait_vmem<0>();
+
+        const uint8_t* st = stage0 + slot * STAGE;
+        u32x4 ka[TP][KS];
+#pragma unroll
+        for (int u = 0; u < TP; ++u)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = 4 * ks + q4;
+                ka[u][ks] = *(const u32x4*)(st + u * KB + (n16 * CPR + (c ^ (n16 % CPR))) * 16);
+            }
+        uint32_t vx[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int off = OFF_V + (16 * dt + n16) * 8 + 2 * q4;
+            vx[dt] = (uint32_t)*(const uint16_t*)(st + off) | ((uint32_t)*(const uint16_t*)(st + off + VB) << 16);
+        }
+        u32x2 ksw[TP];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) ksw[u] = *(const u32x2*)(st + OFF_KS + u * KSB + 8 * q4);
+        // value scales of tokens 4q4 .. 4q4+3, all groups: NG halves per token
+        uint32_t vsr[TP][4 * NVW];
+#pragma unroll
+        for (int u = 0; u < TP; ++u)
+#pragma unroll
+            for (int c = 0; c < NVW; ++c) {
+                const u32x4 v = *(const u32x4*)(st + OFF_VS + u * VSB + 8 * NG * q4 + 16 * c);
+                vsr[u][4 * c] = v.x; vsr[u][4 * c + 1] = v.y; vsr[u][4 * c + 2] = v.z; vsr[u][4 * c + 3] = v.w;
+            }
+        wait_lds_all();
+
+        // ---- scores
+        i32x4_t chi[RB][TP], clo[RB][TP];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int u = 0; u < TP; ++u) {
+                chi[rb][u] = i32x4_t{0, 0, 0, 0};
+                clo[rb][u] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const i32x4_t a = __builtin_bit_cast(i32x4_t, ka[u][ks]);
+                    chi[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qhi[rb][ks]), chi[rb][u], 0, 0, 0);
+                    clo[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qlo[rb][ks]), clo[rb][u], 0, 0, 0);
+                }
+            }
+        const int pg0 = w.pbeg + TP * (wave + WAVES * t);
+        float kf[TP][4];
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            kf[u][0] = h2f((uint16_t)ksw[u].x);
+            kf[u][1] = h2f((uint16_t)(ksw[u].x >> 16));
+            kf[u][2] = h2f((uint16_t)ksw[u].y);
+            kf[u][3] = h2f((uint16_t)(ksw[u].y >> 16));
+        }
+        const bool edge = (pg0 + TP) * 16 > lim_min || pg0 + TP > pend;
+        // the fp16 pairs of this tile's value codes, shared by the row blocks
+        uint32_t pp[RB][4];                    // probabilities (page 0, page 1) per token 4q4 + j
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            float s[TP][4];
+#pragma unroll
+            for (int u = 0; u < TP; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[u][i] = (float)(256 * chi[rb][u][i] + clo[rb][u][i]) * (kf[u][i] * coef[rb]);
+            if (edge) {
+#pragma unroll
+                for (int u = 0; u < TP; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int pos = (pg0 + u) * 16 + 4 * q4 + i;
+                        if (!(pg0 + u < pend && pos < lim[rb])) s[u][i] = kNegInf;
+                    }
+            }
+            float tmax = kNegInf;
+#pragma unroll
+            for (int u = 0; u < TP; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[u][i]);
+            tmax = xgroups_max(tmax);
+            const float m_new = fmaxf(m_run[rb], tmax);
+            const float ref = (m_new == kNegInf) ? 0.0f : m_new;
+            const float alpha = exp2_fast(m_run[rb] - ref);
+            m_run[rb] = m_new;
+            float psum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < TP; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[u][i] = exp2_fast(s[u][i] - ref);
+                    psum += s[u][i];
+                }
+            l_run[rb] = l_run[rb] * alpha + psum;
+            if (__builtin_amdgcn_ballot_w64(alpha < 1.0f) != 0) {
+                float ai[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * q4 + i);   // lane 4q4+i holds that row
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    acc[rb][dt][0] *= ai[0]; acc[rb][dt][1] *= ai[1]; acc[rb][dt][2] *= ai[2]; acc[rb][dt][3] *= ai[3];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                pp[rb][j] = as_u32(__builtin_convertvector(
+                    (float __attribute__((ext_vector_type(2)))){s[0][j], s[1][j]}, f16x2));
+        }
+        // ---- O += P' V, group by group
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            // (page 0, page 1) scale pairs of tokens 4q4 + j for group g
+            uint32_t sp[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int hidx = j * NG + g;                 // half index in a token-major record
+                const int dw = hidx >> 1, h = hidx & 1;
+                const uint32_t sel = (uint32_t)(2 * h) | (uint32_t)(2 * h + 1) << 8 | (uint32_t)(4 + 2 * h) << 16 |
+                                     (uint32_t)(5 + 2 * h) << 24;
+                sp[j] = __builtin_amdgcn_perm(vsr[1][dw], vsr[0][dw], sel);
+            }
+            u32x4 pa[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                pa[rb] = u32x4{as_u32(as_h2(pp[rb][0]) * as_h2(sp[0])), as_u32(as_h2(pp[rb][1]) * as_h2(sp[1])),
+                               as_u32(as_h2(pp[rb][2]) * as_h2(sp[2])), as_u32(as_h2(pp[rb][3]) * as_h2(sp[3]))};
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+                const int dt = 2 * g + dd;
+                uint32_t b[4];
+                v_word_to_f16(vx[dt], b);
+                const f16x8_t B = __builtin_bit_cast(f16x8_t, u32x4{b[0], b[1], b[2], b[3]});
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, pa[rb]), B, acc[rb][dt], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- merge the waves in wave order through one [RW][D] buffer
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = xgroups_sum(l_run[rb]);
+        if (q4 == 0) {
+            s_ml[wave][16 * rb + n16][0] = m_run[rb];
+            s_ml[wave][16 * rb + n16][1] = l_tot;
+        }
+    }
+    __syncthreads();           // every wave is done with its ring: reuse it
+    float* s_o = (float*)&s_stage[0][0][0];
+#pragma unroll
+    for (int wv = 0; wv < WAVES; ++wv) {
+        if (wave == wv) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rl = 16 * rb + 4 * q4 + i;
+                    float M = kNegInf;
+#pragma unroll
+                    for (int u = 0; u < WAVES; ++u) M = fmaxf(M, s_ml[u][rl][0]);
+                    const float f = exp2_fast(s_ml[wave][rl][0] - ((M == kNegInf) ? 0.0f : M));
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        float* dst = s_o + rl * D + 16 * dt + n16;
+                        const float v = acc[rb][dt][i] * f;
+                        *dst = (wv == 0) ? v : *dst + v;
+                    }
+                }
+        }
+        __syncthreads();
+    }
+    for (int e = threadIdx.x; e < RW * D; e += 64 * WAVES) {
+        const int rl = e / D, d = e % D;
+        const int r = r0 + rl;
+        if (r >= p.R) continue;
+        float M = kNegInf;
+#pragma unroll
+        for (int u = 0; u < WAVES; ++u) M = fmaxf(M, s_ml[u][rl][0]);
+        const float ref = (M == kNegInf) ? 0.0f : M;
+        float Ls = 0.0f;
+#pragma unroll
+        for (int u = 0; u < WAVES; ++u) Ls += s_ml[u][rl][1] * exp2_fast(s_ml[u][rl][0] - ref);
+        emit_element<D>(p, w, r, d, M, Ls, s_o[rl * D + d]);
+    }
+    if (p.fused && !p.direct) __syncthreads();
+    fused_tail<D, RW>(p, w, r0, &s_stage[0][0][0], (int)sizeof(s_stage));
+}
+
+template <int D, int RB, int WAVES, int STAGES, bool QBF16>
+hipError_t launch_rows_t(const AttnParams& kp, hipStream_t stream) {
+    const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
+    const int blocks = 8 * ((total + 7) / 8);
+    hipLaunchKernelGGL((attn_rows_kernel<D, RB, WAVES, STAGES, QBF16>), dim3(blocks), dim3(64 * WAVES), 0, stream, kp);
+    return hipGetLastError();
+}
+
 template <int D, int R, int WAVES, int STAGES, bool QBF16>
 hipError_t launch_t(const AttnParams& kp, hipStream_t stream) {
     const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
@@ -421,7 +793,29 @@ LaunchFn pick(int rows, int waves, int stages) {
     }
 }
 
+template <int D, bool QBF16>
+LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
+#define Q8K4V_CASE(RB_, W_, S_) \
+    if (rows_per_wg == 16 * RB_ && waves == W_ && stages == S_) return &launch_rows_t<D, RB_, W_, S_, QBF16>;
+    Q8K4V_CASE(1, 2, 2) Q8K4V_CASE(1, 2, 3) Q8K4V_CASE(1, 4, 2) Q8K4V_CASE(1, 4, 3)
+    Q8K4V_CASE(2, 2, 2) Q8K4V_CASE(2, 2, 3) Q8K4V_CASE(2, 4, 2) Q8K4V_CASE(2, 4, 3)
+#undef Q8K4V_CASE
+    return nullptr;
+}
+
 }  // namespace
+
+int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
+    LaunchFn fn = nullptr;
+    if (head_dim == 128) fn = qbf16 ? pick_rows<128, true>(plan.rows_per_wg, plan.waves, plan.stages)
+                                    : pick_rows<128, false>(plan.rows_per_wg, plan.waves, plan.stages);
+    else fn = qbf16 ? pick_rows<64, true>(plan.rows_per_wg, plan.waves, plan.stages)
+                    : pick_rows<64, false>(plan.rows_per_wg, plan.waves, plan.stages);
+    if (!fn) return fail(Q8K4V_EUNSUPPORTED, "attention: no row-block kernel for this rows/waves/stages combination");
+    const hipError_t e = fn(kp, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return Q8K4V_OK;
+}
 
 int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
     LaunchFn fn = nullptr;

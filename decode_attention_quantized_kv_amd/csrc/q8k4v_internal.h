@@ -43,7 +43,7 @@ struct AttnArgs {
     float softmax_scale;
 };
 
-enum Kernel { kVector = 1, kBlockMfma = 2, kMfma = 3, kDec2 = 4 };
+enum Kernel { kVector = 1, kBlockMfma = 2, kMfma = 3, kDec2 = 4, kRows = 5 };
 
 // Fully resolved launch plan.
 struct Plan {

@@ -86,17 +86,20 @@ typedef struct q8k4v_config {
     int32_t split_pages;     /* if > 0: pages per workgroup split (overrides wgs_per_cu) */
     int32_t tile_pages;      /* pages staged in LDS per wave per step: 1, 2 or 4 (the
                                 MFMA variants fix it: 4 for 2, 2 for 3 and 4)          */
-    int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup (variant 4: 2, 4 or 8)   */
+    int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup (variant 4: 2, 4 or 8;
+                                variant 5: 2 or 4)                                     */
     int32_t fused_combine;   /* 1: the last workgroup of a (sequence, kv head) merges
                                 the splits (needs a zeroed workspace counter area);
                                 0: a separate combine kernel                           */
     int32_t qualified;       /* out of tune_select: 1 measured and admitted, 0 default */
     int32_t variant;         /* 0 auto: 4 for 1, 2, 4, 8 or 16 query rows per kv head,
-                                else 3; 1 vector ALUs (1, 2, 4 or 8 rows); 2 4x4x4 block
+                                else 5; 1 vector ALUs (1, 2, 4 or 8 rows); 2 4x4x4 block
                                 MFMA (4 or 8 rows); 3 16x16 MFMA, 16 or 32 rows per
                                 workgroup (any row count); 4 16x16 MFMA with the rows
-                                replicated across the columns (1, 2, 4, 8 or 16 rows)  */
-    int32_t stages;          /* variant 4: tile buffers per wave in the HBM->LDS ring,
+                                replicated across the columns (1, 2, 4, 8 or 16 rows);
+                                5 16x16 MFMA row blocks with the tile ring, 16 or
+                                32 rows per workgroup (any row count)                  */
+    int32_t stages;          /* variants 4, 5: tile buffers per wave in the HBM->LDS ring,
                                 2 or 3 (prefetch depth stages - 1); 0 default        */
 } q8k4v_config;
 

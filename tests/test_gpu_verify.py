@@ -46,8 +46,11 @@ def test_verify_rows_equal_decodes_on_gpu():
         assert err <= ATOL_SIGMA, (j, err)
 
 
-@pytest.mark.parametrize("cfg", [dict(waves_per_wg=1), dict(waves_per_wg=4), dict(fused_combine=0),
-                                 dict(split_pages=2), dict(wgs_per_cu=6)], ids=str)
+@pytest.mark.parametrize("cfg", [dict(waves_per_wg=2), dict(waves_per_wg=4), dict(fused_combine=1),
+                                 dict(split_pages=2), dict(wgs_per_cu=6), dict(variant=5, stages=3),
+                                 dict(variant=5, waves_per_wg=2, stages=2, fused_combine=1),
+                                 dict(variant=3), dict(variant=3, waves_per_wg=1), dict(variant=3, fused_combine=1)],
+                         ids=str)
 def test_verify_launch_configurations(cfg):
     import decode_attention_quantized_kv_amd as q8
     from tests.gpu_util import run_attention, upload_cache
