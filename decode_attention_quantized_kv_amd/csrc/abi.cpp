@@ -178,8 +178,9 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
             return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");
     } else if (kernel == kRows) {
-        if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4)
-            return fail(Q8K4V_EINVAL, "attention: variant 5 needs 2 or 4 waves per workgroup");
+        if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
+            return fail(Q8K4V_EINVAL, "attention: variant 5 needs 2, 4 or 8 waves per workgroup");
+        if (cfg.waves_per_wg == 8 && cfg.stages != 2) return fail(Q8K4V_EINVAL, "attention: variant 5 with 8 waves needs 2 stages");
     } else if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4) {
         return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
     }

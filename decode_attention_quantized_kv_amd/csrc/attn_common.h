@@ -214,33 +214,80 @@ Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0, void* 
     combine_splits<D, RW>(p, w.b, w.kh, r0, n_eff, scratch, scratch_bytes);
 }
 
+// Emit the merged rows [r0, r0 + RW) of a workgroup, four dimensions per
+// thread: s_M / s_L hold each row's max and sum, s_o [RW][D] its unnormalised
+// output (already on the row's reference).  One split: the normalised output.
+// Several: the split record (m, l, o), with plain stores when a separate
+// combine kernel reads it (the kernel boundary orders them) and write-through
+// stores when the last workgroup merges in this launch.
+template <int D, int RW>
+Q8K4V_DEV void emit_rows(const AttnParams& p, const WorkItem& w, int r0, const float* s_M, const float* s_L,
+                         const float* s_o) {
+    constexpr int NQ = D / 4;
+    const size_t rs = (size_t)p.R * partial_stride<D>();
+    float* split_base = p.partials + ((size_t)w.b * p.H + w.kh) * p.n_splits * rs + w.split * rs;
+    for (int e = threadIdx.x; e < RW * NQ; e += blockDim.x) {
+        const int rl = e / NQ, qc = e % NQ;
+        const int r = r0 + rl;
+        if (r >= p.R) continue;
+        const f32x4 O = *((const f32x4*)(s_o + rl * D) + qc);
+        const float Ls = s_L[rl];
+        if (p.direct) {
+            const float inv = (Ls > 0.0f) ? 1.0f / Ls : 0.0f;
+            *((f32x4*)(p.out + out_index(p, w.b, w.kh, r, D)) + qc) = O * inv;
+            continue;
+        }
+        float* rec = split_base + (size_t)r * partial_stride<D>();
+        if (p.fused) {
+            if (qc == 0) { store_coherent(rec, s_M[rl]); store_coherent(rec + 1, Ls); }
+            store_coherent(rec + 4 + 4 * qc, O.x);
+            store_coherent(rec + 5 + 4 * qc, O.y);
+            store_coherent(rec + 6 + 4 * qc, O.z);
+            store_coherent(rec + 7 + 4 * qc, O.w);
+        } else {
+            if (qc == 0) *(float2*)rec = float2{s_M[rl], Ls};
+            *((f32x4*)(rec + 4) + qc) = O;
+        }
+    }
+}
+
 // Merge the waves of a workgroup (each wave left its running max m, sum l
 // and unnormalised output o in LDS), then emit the rows.
 // `scratch` (scratch_bytes of LDS, 16-byte aligned, s_o may lie in it) is
 // free for the fused combine once the rows are emitted.
 template <int D, int RW, int WAVES>
 Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
-                                const float (*s_ml)[RW][2], const float* s_o /* [WAVES][RW][D] */,
+                                const float (*s_ml)[RW][2], float* s_o /* [WAVES][RW][D] */,
                                 void* scratch, int scratch_bytes) {
+    __shared__ float s_M[RW], s_L[RW], s_f[WAVES][RW];
     __syncthreads();
-    for (int e = threadIdx.x; e < RW * D; e += 64 * WAVES) {
-        const int rl = e / D, d = e % D;
-        const int r = r0 + rl;
-        if (r >= p.R) continue;
+    for (int rl = threadIdx.x; rl < RW; rl += 64 * WAVES) {
         float M = kNegInf;
 #pragma unroll
         for (int wv = 0; wv < WAVES; ++wv) M = fmaxf(M, s_ml[wv][rl][0]);
         const float ref = (M == kNegInf) ? 0.0f : M;
-        float Ls = 0.0f, O = 0.0f;
+        float Ls = 0.0f;
 #pragma unroll
         for (int wv = 0; wv < WAVES; ++wv) {
             const float f = exp2_fast(s_ml[wv][rl][0] - ref);
+            s_f[wv][rl] = f;
             Ls += s_ml[wv][rl][1] * f;
-            O += s_o[(wv * RW + rl) * D + d] * f;
         }
-        emit_element<D>(p, w, r, d, M, Ls, O);
+        s_M[rl] = M;
+        s_L[rl] = Ls;
     }
-    if (p.fused && !p.direct) __syncthreads();   // s_o is read above; the merge reuses it
+    __syncthreads();
+    // waves' outputs on the common reference, summed into wave 0's slot
+    constexpr int NQ = D / 4;
+    for (int e = threadIdx.x; e < RW * NQ; e += 64 * WAVES) {
+        const int rl = e / NQ;
+        f32x4 O = *((const f32x4*)s_o + e) * s_f[0][rl];
+#pragma unroll
+        for (int wv = 1; wv < WAVES; ++wv) O += *((const f32x4*)(s_o + wv * RW * D) + e) * s_f[wv][rl];
+        *((f32x4*)s_o + e) = O;
+    }
+    __syncthreads();
+    emit_rows<D, RW>(p, w, r0, s_M, s_L, s_o);
     fused_tail<D, RW>(p, w, r0, scratch, scratch_bytes);
 }
 

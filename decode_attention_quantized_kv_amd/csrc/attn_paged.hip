@@ -703,6 +703,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
     }
 
     // ---- merge the waves in wave order through one [RW][D] buffer
+    __shared__ float s_M[RW], s_L[RW], s_f[WAVES][RW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = xgroups_sum(l_run[rb]);
@@ -712,6 +713,22 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
         }
     }
     __syncthreads();           // every wave is done with its ring: reuse it
+    for (int rl = threadIdx.x; rl < RW; rl += 64 * WAVES) {
+        float M = kNegInf;
+#pragma unroll
+        for (int u = 0; u < WAVES; ++u) M = fmaxf(M, s_ml[u][rl][0]);
+        const float ref = (M == kNegInf) ? 0.0f : M;
+        float Ls = 0.0f;
+#pragma unroll
+        for (int u = 0; u < WAVES; ++u) {
+            const float f = exp2_fast(s_ml[u][rl][0] - ref);
+            s_f[u][rl] = f;
+            Ls += s_ml[u][rl][1] * f;
+        }
+        s_M[rl] = M;
+        s_L[rl] = Ls;
+    }
+    __syncthreads();
     float* s_o = (float*)&s_stage[0][0][0];
 #pragma unroll
     for (int wv = 0; wv < WAVES; ++wv) {
@@ -721,10 +738,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rl = 16 * rb + 4 * q4 + i;
-                    float M = kNegInf;
-#pragma unroll
-                    for (int u = 0; u < WAVES; ++u) M = fmaxf(M, s_ml[u][rl][0]);
-                    const float f = exp2_fast(s_ml[wave][rl][0] - ((M == kNegInf) ? 0.0f : M));
+                    const float f = s_f[wave][rl];
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
                         float* dst = s_o + rl * D + 16 * dt + n16;
@@ -735,20 +749,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
         }
         __syncthreads();
     }
-    for (int e = threadIdx.x; e < RW * D; e += 64 * WAVES) {
-        const int rl = e / D, d = e % D;
-        const int r = r0 + rl;
-        if (r >= p.R) continue;
-        float M = kNegInf;
-#pragma unroll
-        for (int u = 0; u < WAVES; ++u) M = fmaxf(M, s_ml[u][rl][0]);
-        const float ref = (M == kNegInf) ? 0.0f : M;
-        float Ls = 0.0f;
-#pragma unroll
-        for (int u = 0; u < WAVES; ++u) Ls += s_ml[u][rl][1] * exp2_fast(s_ml[u][rl][0] - ref);
-        emit_element<D>(p, w, r, d, M, Ls, s_o[rl * D + d]);
-    }
-    if (p.fused && !p.direct) __syncthreads();
+    emit_rows<D, RW>(p, w, r0, s_M, s_L, s_o);
     fused_tail<D, RW>(p, w, r0, &s_stage[0][0][0], (int)sizeof(s_stage));
 }
 
@@ -799,6 +800,7 @@ LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
     if (rows_per_wg == 16 * RB_ && waves == W_ && stages == S_) return &launch_rows_t<D, RB_, W_, S_, QBF16>;
     Q8K4V_CASE(1, 2, 2) Q8K4V_CASE(1, 2, 3) Q8K4V_CASE(1, 4, 2) Q8K4V_CASE(1, 4, 3)
     Q8K4V_CASE(2, 2, 2) Q8K4V_CASE(2, 2, 3) Q8K4V_CASE(2, 4, 2) Q8K4V_CASE(2, 4, 3)
+    Q8K4V_CASE(1, 8, 2) Q8K4V_CASE(2, 8, 2)
 #undef Q8K4V_CASE
     return nullptr;
 }
