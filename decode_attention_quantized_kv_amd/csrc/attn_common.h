@@ -215,12 +215,12 @@ Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0, void* 
 }
 
 // Emit the merged rows [r0, r0 + RW) of a workgroup, four dimensions per
-// thread: s_M / s_L hold each row's max and sum, s_o [RW][D] its unnormalised
+// thread: s_M / s_L hold each row's max and sum, s_o [RW][SO_STRIDE] its unnormalised
 // output (already on the row's reference).  One split: the normalised output.
 // Several: the split record (m, l, o), with plain stores when a separate
 // combine kernel reads it (the kernel boundary orders them) and write-through
 // stores when the last workgroup merges in this launch.
-template <int D, int RW>
+template <int D, int RW, int SO_STRIDE = D>
 Q8K4V_DEV void emit_rows(const AttnParams& p, const WorkItem& w, int r0, const float* s_M, const float* s_L,
                          const float* s_o) {
     constexpr int NQ = D / 4;
@@ -230,7 +230,7 @@ Q8K4V_DEV void emit_rows(const AttnParams& p, const WorkItem& w, int r0, const f
         const int rl = e / NQ, qc = e % NQ;
         const int r = r0 + rl;
         if (r >= p.R) continue;
-        const f32x4 O = *((const f32x4*)(s_o + rl * D) + qc);
+        const f32x4 O = *((const f32x4*)(s_o + rl * SO_STRIDE) + qc);
         const float Ls = s_L[rl];
         if (p.direct) {
             const float inv = (Ls > 0.0f) ? 1.0f / Ls : 0.0f;

@@ -418,7 +418,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
     constexpr int RW = 16 * RB;                // rows per workgroup
     constexpr int NVW = NG / 2;                // 32-bit words of one token's value scales
     static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
-    static_assert(RW * D * 4 <= WAVES * STAGES * STAGE, "the merge buffer reuses the tile ring");
+    constexpr int SOS = D + 4;                 // merge-buffer row stride: lane groups 4 rows apart
+                                               // land 16 banks apart
+    static_assert(RW * SOS * 4 <= WAVES * STAGES * STAGE, "the merge buffer reuses the tile ring");
 
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES][STAGES][STAGE];
     __shared__ float s_ml[WAVES][RW][2];
@@ -741,7 +743,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
                     const float f = s_f[wave][rl];
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        float* dst = s_o + rl * D + 16 * dt + n16;
+                        float* dst = s_o + rl * SOS + 16 * dt + n16;
                         const float v = acc[rb][dt][i] * f;
                         *dst = (wv == 0) ? v : *dst + v;
                     }
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
         }
         __syncthreads();
     }
-    emit_rows<D, RW>(p, w, r0, s_M, s_L, s_o);
+    emit_rows<D, RW, SOS>(p, w, r0, s_M, s_L, s_o);
     fused_tail<D, RW>(p, w, r0, &s_stage[0][0][0], (int)sizeof(s_stage));
 }
 
