@@ -731,10 +731,18 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
         s_L[rl] = Ls;
     }
     __syncthreads();
+    // two rounds into NB = WAVES/2 buffers (upper half of the waves writes,
+    // lower half adds), then one pass sums the buffers: fixed order, three
+    // barriers whatever the wave count
+    constexpr int NB = WAVES / 2;
+    constexpr int BUF = RW * SOS;
+    static_assert(NB * BUF * 4 <= WAVES * STAGES * STAGE, "merge buffers reuse the tile ring");
     float* s_o = (float*)&s_stage[0][0][0];
 #pragma unroll
-    for (int wv = 0; wv < WAVES; ++wv) {
-        if (wave == wv) {
+    for (int round = 0; round < 2; ++round) {
+        const bool mine = round == 0 ? wave >= NB : wave < NB;
+        if (mine) {
+            float* buf = s_o + (wave % NB) * BUF;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -743,11 +751,22 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
                     const float f = s_f[wave][rl];
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        float* dst = s_o + rl * SOS + 16 * dt + n16;
+                        float* dst = buf + rl * SOS + 16 * dt + n16;
                         const float v = acc[rb][dt][i] * f;
-                        *dst = (wv == 0) ? v : *dst + v;
+                        *dst = (round == 0) ? v : *dst + v;
                     }
                 }
+        }
+        __syncthreads();
+    }
+    if (NB > 1) {
+        for (int e = threadIdx.x; e < RW * (D / 4); e += 64 * WAVES) {
+            const int rl = e / (D / 4), c4 = e % (D / 4);
+            f32x4* d0 = (f32x4*)(s_o + rl * SOS) + c4;
+            f32x4 sum = *d0;
+#pragma unroll
+            for (int b = 1; b < NB; ++b) sum += *((const f32x4*)(s_o + b * BUF + rl * SOS) + c4);
+            *d0 = sum;
         }
         __syncthreads();
     }
