@@ -74,11 +74,12 @@ int32_t device_cu_count() {
 namespace {
 bool dec2_rows(int32_t rows) { return rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16; }
 
-// launch shape defaults per kernel
-void kernel_defaults(int32_t kernel, q8k4v_config* c) {
+// launch shape defaults per kernel; the row-block kernel takes 8 waves once
+// two row blocks share the page stream (more than 16 rows per kv head)
+void kernel_defaults(int32_t kernel, int32_t rows, q8k4v_config* c) {
     switch (kernel) {
         case kDec2: c->wgs_per_cu = 1; c->waves_per_wg = 4; c->stages = 2; c->tile_pages = 2; break;
-        case kRows: c->wgs_per_cu = 1; c->waves_per_wg = 4; c->stages = 2; c->tile_pages = 2; break;
+        case kRows: c->wgs_per_cu = 1; c->waves_per_wg = rows > 16 ? 8 : 4; c->stages = 2; c->tile_pages = 2; break;
         case kMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 2; break;
         case kBlockMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
         default: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
@@ -91,7 +92,7 @@ int32_t auto_kernel(int32_t rows) { return dec2_rows(rows) ? kDec2 : kRows; }
 q8k4v_config default_config(int32_t rows) {
     q8k4v_config c;
     std::memset(&c, 0, sizeof(c));
-    kernel_defaults(auto_kernel(rows), &c);
+    kernel_defaults(auto_kernel(rows), rows, &c);
     c.split_pages = 0;
     c.fused_combine = 0;
     c.qualified = 0;
@@ -170,10 +171,11 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     }
     q8k4v_config kd;
     std::memset(&kd, 0, sizeof(kd));
-    kernel_defaults(kernel, &kd);
+    kernel_defaults(kernel, rows, &kd);
     if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = kd.wgs_per_cu;
-    if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = kd.waves_per_wg;
     if (cfg.stages <= 0) cfg.stages = kd.stages;
+    if (cfg.waves_per_wg <= 0)   // 8 row-block waves fit only a two-stage ring
+        cfg.waves_per_wg = (kernel == kRows && cfg.stages != 2) ? 4 : kd.waves_per_wg;
     if (kernel == kDec2) {
         if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
             return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");

@@ -86,8 +86,9 @@ typedef struct q8k4v_config {
     int32_t split_pages;     /* if > 0: pages per workgroup split (overrides wgs_per_cu) */
     int32_t tile_pages;      /* pages staged in LDS per wave per step: 1, 2 or 4 (the
                                 MFMA variants fix it: 4 for 2, 2 for 3 and 4)          */
-    int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup (variant 4: 2, 4 or 8;
-                                variant 5: 2 or 4)                                     */
+    int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup (variants 4 and 5: 2, 4
+                                or 8; variant 5 with 8 waves needs 2 stages). Default
+                                4, or 8 for variant 5 above 16 rows per kv head      */
     int32_t fused_combine;   /* 1: the last workgroup of a (sequence, kv head) merges
                                 the splits (needs a zeroed workspace counter area);
                                 0: a separate combine kernel                           */
