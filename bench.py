@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--config", default="", help="JSON dict of launch config fields")
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention launches (profiling)")
     ap.add_argument("--contiguous-pages", action="store_true", help="identity page table (profiling)")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="shared-prefix workload: plain decode instead of the prefix cascade")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -122,13 +124,22 @@ def main() -> int:
         cfg = vcfg if w.n_draft else dcfg
         tuned = cfg.as_dict()
     nd = w.n_draft
-    ws = torch.zeros(max(16, q8.workspace_bytes(B, Hq, H, D, msl, nd, cfg)), dtype=torch.uint8, device=dev)
+    # sessions over one shared prefix run the prefix cascade
+    n_pref = 0 if (nd or args.no_cascade) else w.shared_prefix // 16
+    if n_pref:
+        nws = q8.prefix_workspace_bytes(B, Hq, H, D, msl, n_pref, cfg)
+    else:
+        nws = q8.workspace_bytes(B, Hq, H, D, msl, nd, cfg)
+    ws = torch.zeros(max(16, nws), dtype=torch.uint8, device=dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
     def attend(c):
         if nd:
             q8.attn_verify_q8k4v(c, q, seq_lens, msl, page_table, w.softmax_scale, out=out, cfg=cfg, workspace=ws)
+        elif n_pref:
+            q8.attn_decode_prefix_q8k4v(c, q, seq_lens, msl, page_table, n_pref, w.softmax_scale, out=out, cfg=cfg,
+                                        workspace=ws)
         else:
             q8.attn_decode_q8k4v(c, q, seq_lens, msl, page_table, w.softmax_scale, out=out, cfg=cfg, workspace=ws)
 
@@ -209,11 +220,14 @@ def main() -> int:
         "config": {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": H, "head_dim": D,
                    "context": int(w.seq_lens.max()), "n_seqs": B, "n_draft": nd, "page_size": 16,
                    "rotating_layer_caches": layers, "layer_cache_bytes": layer_bytes,
-                   "launch_config": tuned or (cfg.as_dict() if cfg else "default")},
+                   "launch_config": tuned or (cfg.as_dict() if cfg else "default"),
+                   "shared_prefix_pages": n_pref},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(w.name, nd),
-                     "kernel": ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v")
-                               + " launch (split-K attention kernel + LSE combine kernel)",
+                     "kernel": ("attn_decode_prefix_q8k4v launch (prefix-pass kernel + suffix-pass kernel"
+                                " + LSE combine kernel)" if n_pref else
+                                ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v")
+                                + " launch (split-K attention kernel + LSE combine kernel)"),
                      "algorithmic_bytes": attn_bytes, "avg_launch_us": round(ms_attn * 1e3, 3)},
         "step_bytes": step_bytes,
         "wall_s": round(wall, 3),

@@ -90,6 +90,11 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.attn_decode_q8k4v.restype = i32
     lib.attn_decode_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, vp, i32, vp, i32,
                                       C.c_float, C.POINTER(Config), vp, sz, vp]
+    lib.attn_decode_prefix_q8k4v.restype = i32
+    lib.attn_decode_prefix_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, vp, i32, vp, i32, i32,
+                                             C.c_float, C.POINTER(Config), vp, sz, vp]
+    lib.q8k4v_prefix_workspace_bytes.restype = sz
+    lib.q8k4v_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(Config)]
     lib.attn_verify_q8k4v.restype = i32
     lib.attn_verify_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, i32, vp, i32, vp, i32,
                                       C.c_float, C.POINTER(Config), vp, sz, vp]
@@ -216,6 +221,38 @@ def attn_decode_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_t
     return out
 
 
+def prefix_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_seq_len: int,
+                           n_prefix_pages: int, cfg: Optional[Config] = None) -> int:
+    lib = load_library()
+    return int(lib.q8k4v_prefix_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                n_prefix_pages, C.byref(cfg) if cfg is not None else None))
+
+
+def attn_decode_prefix_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_table, n_prefix_pages: int,
+                             softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
+                             workspace=None, stream=None):
+    """Decode of sessions sharing their first ``n_prefix_pages`` pages (same
+    physical ids in every row of ``page_table``): ``q [B][Hq][D]`` ->
+    ``out [B][Hq][D]`` float32, as :func:`attn_decode_q8k4v`."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = _workspace(prefix_workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len,
+                                                      n_prefix_pages, cfg), q.device)
+    rc = lib.attn_decode_prefix_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq,
+                                      _ptr(seq_lens), int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+                                      int(n_prefix_pages), float(softmax_scale),
+                                      C.byref(cfg) if cfg is not None else None,
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("attn_decode_prefix_q8k4v", rc)
+    return out
+
+
 def attn_verify_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_table,
                       softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
                       workspace=None, stream=None):
@@ -278,5 +315,6 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
     return table[0], table[1], report
 
 
-__all__ = ["kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select", "workspace_bytes",
+__all__ = ["kv_quant_append", "attn_decode_q8k4v", "attn_decode_prefix_q8k4v", "attn_verify_q8k4v", "tune_select",
+           "workspace_bytes", "prefix_workspace_bytes",
            "PagedKVCache", "Config", "make_config", "load_library", "version", "Q8K4VError", "LIB_PATH"]

@@ -24,6 +24,7 @@ int32_t launch_mfma(const AttnParams& kp, const Plan& plan, int head_dim, bool q
 int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
+int32_t launch_combine_cascade(const AttnParams& kp, int head_dim, hipStream_t stream);
 
 namespace {
 thread_local std::string g_last_error;
@@ -174,15 +175,13 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     kernel_defaults(kernel, rows, &kd);
     if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = kd.wgs_per_cu;
     if (cfg.stages <= 0) cfg.stages = kd.stages;
-    if (cfg.waves_per_wg <= 0)   // 8 row-block waves fit only a two-stage ring
-        cfg.waves_per_wg = (kernel == kRows && cfg.stages != 2) ? 4 : kd.waves_per_wg;
+    if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = kd.waves_per_wg;
     if (kernel == kDec2) {
         if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
             return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");
     } else if (kernel == kRows) {
         if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
             return fail(Q8K4V_EINVAL, "attention: variant 5 needs 2, 4 or 8 waves per workgroup");
-        if (cfg.waves_per_wg == 8 && cfg.stages != 2) return fail(Q8K4V_EINVAL, "attention: variant 5 with 8 waves needs 2 stages");
     } else if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4) {
         return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
     }
@@ -226,6 +225,9 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     }
     if ((kernel == kDec2 || kernel == kRows) && plan->split_pages > 64 * cfg.waves_per_wg)
         return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long for variants 4 and 5 (more than 1024 splits)");
+    // a multiple of 8 splits lets the kernels deal each sequence's splits
+    // round robin over the 8 XCDs (the extra splits hold no pages)
+    if (plan->n_splits > 1) plan->n_splits = round_up(plan->n_splits, 8);
     plan->fused_combine = (plan->n_splits > 1 && cfg.fused_combine) ? 1 : 0;
     const size_t rec = (size_t)(a.cache->head_dim + 4) * sizeof(float);
     plan->partial_bytes = plan->n_splits > 1 ? (size_t)a.n_seqs * H * plan->n_splits * rows * rec : 0;
@@ -238,13 +240,11 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
 
 size_t plan_workspace(const Plan& p) { return p.partial_bytes + p.counter_bytes; }
 
-int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
-    const size_t need = plan_workspace(plan);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(Q8K4V_EWORKSPACE, "attention: workspace needs " + std::to_string(need) + " bytes");
+namespace {
+// Kernel parameters of one plain launch (no page offsets, no cascade).
+AttnParams launch_params(const AttnArgs& a, const Plan& plan, void* workspace) {
     const q8k4v_cache& c = *a.cache;
-    AttnParams kp;
+    AttnParams kp{};
     kp.k_codes = c.k_codes;
     kp.k_scales = c.k_scales;
     kp.v_codes = c.v_codes;
@@ -268,18 +268,124 @@ int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, s
     kp.scale_log2 = a.softmax_scale * kLog2e;
     kp.direct = plan.n_splits == 1;
     kp.fused = plan.fused_combine;
-    const bool bf = a.q_dtype == Q8K4V_BF16;
-    int32_t rc;
+    return kp;
+}
+
+int32_t launch_kernel(const AttnParams& kp, const Plan& plan, int head_dim, bool bf, hipStream_t stream) {
     switch (plan.kernel) {
-        case kVector: rc = launch_valu(kp, plan, c.head_dim, bf, stream); break;
-        case kBlockMfma: rc = launch_bmfma(kp, plan, c.head_dim, bf, stream); break;
-        case kDec2: rc = launch_dec2(kp, plan, c.head_dim, bf, stream); break;
-        case kRows: rc = launch_rows(kp, plan, c.head_dim, bf, stream); break;
-        default: rc = launch_mfma(kp, plan, c.head_dim, bf, stream); break;
+        case kVector: return launch_valu(kp, plan, head_dim, bf, stream);
+        case kBlockMfma: return launch_bmfma(kp, plan, head_dim, bf, stream);
+        case kDec2: return launch_dec2(kp, plan, head_dim, bf, stream);
+        case kRows: return launch_rows(kp, plan, head_dim, bf, stream);
+        default: return launch_mfma(kp, plan, head_dim, bf, stream);
     }
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    const size_t need = plan_workspace(plan);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(Q8K4V_EWORKSPACE, "attention: workspace needs " + std::to_string(need) + " bytes");
+    const AttnParams kp = launch_params(a, plan, workspace);
+    const int D = a.cache->head_dim;
+    const int32_t rc = launch_kernel(kp, plan, D, a.q_dtype == Q8K4V_BF16, stream);
     if (rc != Q8K4V_OK) return rc;
-    if (!kp.direct && !kp.fused) return launch_combine(kp, c.head_dim, plan.rows_per_wg, stream);
+    if (!kp.direct && !kp.fused) return launch_combine(kp, D, plan.rows_per_wg, stream);
     return Q8K4V_OK;
+}
+
+// ---- shared-prefix cascade ------------------------------------------------
+// Sessions whose first n_prefix_pages logical pages are the same physical
+// pages (a shared prompt prefix, blog.123qwe.co.kr/?p=3927, section 5) are
+// decoded in three launches: a prefix pass of the row-block kernel over one
+// virtual sequence -- the shared pages, read once for all sessions -- whose
+// query rows are every session's rows (session j as "draft" j, no causal
+// edge inside the prefix); a suffix pass, the plain decode plan over each
+// session's pages from n_prefix_pages on; and a combine that merges both
+// record sets per (session, q head) by log-sum-exp.
+int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config* cfg, CascadePlan* cp) {
+    if (n_pref < 1 || n_pref > a.max_pages || (int64_t)n_pref * Q8K4V_PAGE_SIZE > a.max_seq_len)
+        return fail(Q8K4V_EINVAL, "attention: n_prefix_pages must be in 1 .. min(max_pages, max_seq_len / 16)");
+    AttnArgs as = a;
+    as.max_seq_len = a.max_seq_len - n_pref * Q8K4V_PAGE_SIZE;
+    int32_t rc = make_plan(as, cfg, &cp->suf);
+    if (rc != Q8K4V_OK) return rc;
+    const int32_t H = a.cache->num_kv_heads;
+    const int32_t G = a.num_q_heads / H;
+    const size_t rec = (size_t)(a.cache->head_dim + 4) * sizeof(float);
+    Plan& sp = cp->suf;
+    sp.fused_combine = 0;
+    sp.counter_bytes = 0;
+    sp.partial_bytes = round256((size_t)a.n_seqs * H * sp.n_splits * sp.rows * rec);
+
+    Plan& pp = cp->pre;
+    const int64_t rows = (int64_t)a.n_seqs * G;
+    if (rows > kMaxPrefixRows)
+        return fail(Q8K4V_EUNSUPPORTED, "attention: the prefix pass takes at most " + std::to_string(kMaxPrefixRows) +
+                                            " query rows per kv head (n_seqs * group)");
+    pp = Plan{};
+    pp.rows = (int32_t)rows;
+    pp.kernel = kRows;
+    pp.mfma = 1;
+    pp.tile_pages = 2;
+    pp.waves = rows > 16 ? 8 : 4;
+    pp.stages = 2;
+    pp.rows_per_wg = rows > 16 ? 32 : 16;
+    pp.row_chunks = (pp.rows + pp.rows_per_wg - 1) / pp.rows_per_wg;
+    const int32_t unit = pp.tile_pages * pp.waves;
+    const int64_t per = (int64_t)H * pp.row_chunks;
+    const int64_t splits = std::max<int64_t>(1, (device_cu_count() + per - 1) / per);
+    int32_t spp = round_up((int32_t)((n_pref + splits - 1) / splits), unit);
+    spp = std::min(std::max(spp, unit), 64 * pp.waves);
+    pp.split_pages = spp;
+    pp.n_splits = (n_pref + spp - 1) / spp;
+    if (pp.n_splits > 1) pp.n_splits = round_up(pp.n_splits, 8);
+    pp.fused_combine = 0;
+    pp.counter_bytes = 0;
+    pp.partial_bytes = round256((size_t)H * pp.n_splits * pp.rows * rec);
+    if (per * pp.n_splits + 8 > 0x7FFFFFFFLL) return fail(Q8K4V_EINVAL, "attention: launch too large");
+    return Q8K4V_OK;
+}
+
+int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    const size_t need = cp.pre.partial_bytes + cp.suf.partial_bytes;
+    if (!workspace || workspace_bytes < need)
+        return fail(Q8K4V_EWORKSPACE, "attention: workspace needs " + std::to_string(need) + " bytes");
+    const int D = a.cache->head_dim;
+    const bool bf = a.q_dtype == Q8K4V_BF16;
+    float* pre_part = (float*)workspace;
+    float* suf_part = (float*)((char*)workspace + cp.pre.partial_bytes);
+
+    AttnParams pre = launch_params(a, cp.pre, pre_part);
+    pre.partials = pre_part;
+    pre.n_seqs = 1;                 // page table row 0 holds the shared pages
+    pre.W = a.n_seqs;               // session j's rows are "draft" j
+    pre.R = cp.pre.rows;
+    pre.page_cap = n_pref;
+    pre.cascade = 1;
+    pre.direct = 0;
+    pre.fused = 0;
+    int32_t rc = launch_rows(pre, cp.pre, D, bf, stream);
+    if (rc != Q8K4V_OK) return rc;
+
+    AttnParams suf = launch_params(a, cp.suf, suf_part);
+    suf.partials = suf_part;
+    suf.page_lo = n_pref;
+    suf.cascade = 1;
+    suf.direct = 0;
+    suf.fused = 0;
+    rc = launch_kernel(suf, cp.suf, D, bf, stream);
+    if (rc != Q8K4V_OK) return rc;
+
+    suf.pre_partials = pre_part;
+    suf.pre_splits = cp.pre.n_splits;
+    suf.pre_eff = (n_pref + cp.pre.split_pages - 1) / cp.pre.split_pages;
+    suf.pre_R = cp.pre.rows;
+    return launch_combine_cascade(suf, D, stream);
 }
 
 }  // namespace q8k4v
@@ -308,19 +414,19 @@ int32_t kv_quant_append(const q8k4v_cache* cache, const void* k_new, const void*
     return launch_append(a, stream);
 }
 
-size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                             int32_t max_seq_len, int32_t n_draft, const q8k4v_config* cfg) {
-    q8k4v_cache fake;
-    fake.num_pages = 1;
-    fake.num_kv_heads = num_kv_heads;
-    fake.head_dim = head_dim;
-    fake.page_size = Q8K4V_PAGE_SIZE;
-    fake.k_codes = (int8_t*)1;
-    fake.k_scales = (uint16_t*)1;
-    fake.v_codes = (uint8_t*)1;
-    fake.v_scales = (uint16_t*)1;
+// Launch arguments with placeholder pointers, for workspace queries.
+static AttnArgs shape_args(q8k4v_cache* fake, int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t max_seq_len, int32_t n_draft) {
+    fake->num_pages = 1;
+    fake->num_kv_heads = num_kv_heads;
+    fake->head_dim = head_dim;
+    fake->page_size = Q8K4V_PAGE_SIZE;
+    fake->k_codes = (int8_t*)1;
+    fake->k_scales = (uint16_t*)1;
+    fake->v_codes = (uint8_t*)1;
+    fake->v_scales = (uint16_t*)1;
     AttnArgs a{};
-    a.cache = &fake;
+    a.cache = fake;
     a.q = (const void*)1;
     a.q_dtype = Q8K4V_BF16;
     a.out = (float*)1;
@@ -332,10 +438,32 @@ size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv
     a.page_table = (const int32_t*)1;
     a.max_pages = std::max(1, (max_seq_len + 15) / 16);
     a.softmax_scale = 1.0f;
+    return a;
+}
+
+size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_seq_len, int32_t n_draft, const q8k4v_config* cfg) {
+    q8k4v_cache fake;
+    const AttnArgs a = shape_args(&fake, n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, n_draft);
     Plan p;
     std::string saved = g_last_error;
     if (make_plan(a, cfg, &p) != Q8K4V_OK) { g_last_error = saved; return 0; }
     return plan_workspace(p);
+}
+
+size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_seq_len, int32_t n_prefix_pages, const q8k4v_config* cfg) {
+    if (n_prefix_pages == 0)
+        return q8k4v_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 0, cfg);
+    q8k4v_cache fake;
+    const AttnArgs a = shape_args(&fake, n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 1);
+    CascadePlan cp;
+    std::string saved = g_last_error;
+    if (make_plan(a, cfg, &cp.suf) != Q8K4V_OK || make_cascade_plan(a, n_prefix_pages, cfg, &cp) != Q8K4V_OK) {
+        g_last_error = saved;
+        return 0;
+    }
+    return cp.pre.partial_bytes + cp.suf.partial_bytes;
 }
 
 static int32_t attention_entry(const char* name, const q8k4v_cache* cache, const void* q, int32_t q_dtype,
@@ -361,6 +489,28 @@ int32_t attn_decode_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dty
     return attention_entry("attn_decode_q8k4v", cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens,
                            max_seq_len, page_table, max_pages, softmax_scale, cfg, workspace, workspace_bytes,
                            stream);
+}
+
+int32_t attn_decode_prefix_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out,
+                                 int32_t n_seqs, int32_t num_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
+                                 const int32_t* page_table, int32_t max_pages, int32_t n_prefix_pages,
+                                 float softmax_scale, const q8k4v_config* cfg, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    const char* name = "attn_decode_prefix_q8k4v";
+    if (n_prefix_pages < 0) return fail(Q8K4V_EINVAL, std::string(name) + ": n_prefix_pages must be >= 0");
+    if (n_prefix_pages == 0)
+        return attention_entry(name, cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens, max_seq_len,
+                               page_table, max_pages, softmax_scale, cfg, workspace, workspace_bytes, stream);
+    AttnArgs a{cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens, max_seq_len,
+               page_table, max_pages, softmax_scale};
+    CascadePlan cp;
+    int32_t rc = make_plan(a, cfg, &cp.suf);        // validates the shape as a decode launch
+    if (rc == Q8K4V_OK) rc = make_cascade_plan(a, n_prefix_pages, cfg, &cp);
+    if (rc != Q8K4V_OK) {
+        g_last_error = std::string(name) + ": " + g_last_error;
+        return rc;
+    }
+    return launch_cascade(a, n_prefix_pages, cp, workspace, workspace_bytes, stream);
 }
 
 int32_t attn_verify_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out, int32_t n_seqs,

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bmfma_kernel(const AttnParams
     WorkItem w;
     if (!work_item(p, w)) return;
     if (w.pbeg >= w.pend) {
-        if (w.split == 0) write_zero_rows<D>(p, w, 0, R);
+        if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, 0, R);
         return;
     }
     const int blk = lane >> 2;             // MFMA block

@@ -24,6 +24,17 @@ struct AttnParams {
     float scale_log2;                  // softmax scale * log2(e)
     int32_t direct;                    // one split: write normalised output
     int32_t fused;                     // last workgroup merges the splits
+    // Page ranges of the shared-prefix cascade (0 for a plain launch):
+    // page_lo is the first logical page of every split range; page_cap > 0
+    // makes every sequence exactly page_cap pages long with no causal edge
+    // inside them (the prefix pass over pages all sessions share).
+    int32_t page_lo, page_cap;
+    int32_t cascade;                   // pass of a cascade: partials only
+    // prefix-pass partials, read by the cascade combine:
+    // [H][pre_splits][pre_R][D + 4], row b * G + g of session b; the first
+    // pre_eff splits hold pages
+    const float* __restrict__ pre_partials;
+    int32_t pre_splits, pre_eff, pre_R;
 };
 
 constexpr float kNegInf = -__builtin_inff();
@@ -46,23 +57,43 @@ struct WorkItem {
     int b, kh, split, rchunk, L, npages, pbeg, pend;
 };
 
-// Work items (sequence, split, kv head, row chunk) are numbered so that
-// consecutive items are the kv heads of one split; the dispatcher hands
-// workgroup i to XCD i % 8, so item = xcd * per_xcd + i / 8 keeps a split's
-// heads (which share the lines of the key-scale pool) on one XCD's L2.
+// Work items are (sequence, split, kv head, row chunk); the dispatcher hands
+// workgroup i to XCD i % 8.  The kv heads and row chunks of one (sequence,
+// split) -- which share the lines of the key-scale pool -- stay on one XCD's
+// L2.  With a split count that is a multiple of 8, split s of sequence b goes
+// to XCD (s + b) mod 8: every sequence's splits are dealt round robin over
+// the XCDs, starting at a different XCD per sequence, so a ragged batch
+// loads the XCDs evenly.  Otherwise XCD x takes the x-th eighth of the items
+// in order.
 Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w) {
-    const int total = p.n_seqs * p.H * p.n_splits * p.row_chunks;
-    const int per_xcd = (total + 7) >> 3;
-    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (item >= total) return false;
-    w.rchunk = item % p.row_chunks;
-    const int it = item / p.row_chunks;
-    w.kh = it % p.H;
-    w.split = (it / p.H) % p.n_splits;
-    w.b = it / (p.H * p.n_splits);
-    w.L = p.seq_lens[w.b];
-    w.npages = (w.L + 15) >> 4;
-    w.pbeg = w.split * p.split_pages;
+    const int C = p.H * p.row_chunks;          // items per (sequence, split)
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    int inner;
+    if ((p.n_splits & 7) == 0) {
+        const int S8 = p.n_splits >> 3;        // splits per sequence and XCD
+        inner = j % C;
+        const int t = j / C;
+        w.b = t / S8;
+        if (w.b >= p.n_seqs) return false;
+        w.split = ((x - w.b) & 7) + 8 * (t % S8);
+    } else {
+        const int total = p.n_seqs * p.n_splits * C;
+        const int item = x * ((total + 7) >> 3) + j;
+        if (item >= total) return false;
+        inner = item % C;
+        w.split = (item / C) % p.n_splits;
+        w.b = item / (C * p.n_splits);
+    }
+    w.rchunk = inner % p.row_chunks;
+    w.kh = inner / p.row_chunks;
+    if (p.page_cap > 0) {
+        w.npages = p.page_cap;
+        w.L = 16 * p.page_cap + p.W - 1;       // row j's causal limit 16 page_cap + j: no edge inside
+    } else {
+        w.L = p.seq_lens[w.b];
+        w.npages = (w.L + 15) >> 4;
+    }
+    w.pbeg = p.page_lo + w.split * p.split_pages;
     w.pend = min(w.npages, w.pbeg + p.split_pages);
     return true;
 }
@@ -199,7 +230,7 @@ template <int D, int RW>
 Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0, void* scratch, int scratch_bytes) {
     if (p.direct || !p.fused) return;
     __shared__ int s_last;
-    const int n_eff = (w.npages + p.split_pages - 1) / p.split_pages;
+    const int n_eff = (max(0, w.npages - p.page_lo) + p.split_pages - 1) / p.split_pages;
     // every thread's write-through stores have completed before the barrier
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -313,7 +344,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     const int b = blockIdx.x / (p.R * p.H);
     const int L = p.seq_lens[b];
     const int npages = (L + 15) >> 4;
-    const int n_eff = min(p.n_splits, (npages + p.split_pages - 1) / p.split_pages);
+    const int n_eff = min(p.n_splits, (max(0, npages - p.page_lo) + p.split_pages - 1) / p.split_pages);
     const size_t rs = (size_t)p.R * partial_stride<D>();
     const float* base = p.partials + ((size_t)b * p.H + kh) * p.n_splits * rs + (size_t)r * partial_stride<D>();
     float M = kNegInf, Ls = 0.0f;
@@ -376,6 +407,96 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
         const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
         f32x4* dst = (f32x4*)(p.out + out_index(p, b, kh, r, D)) + t;
         *dst = sum * inv;
+    }
+}
+
+// Combine of the shared-prefix cascade: one 256-thread workgroup per
+// (b, kh, g) of a decode launch.  Row (b, g) has two record sets: the prefix
+// pass's first pre_eff records (row b * G + g of each [pre_R] block) and the
+// suffix pass's splits of sequence b, of which those past its last page are
+// masked.  Both sets are walked as one list of pre_eff + n_splits records,
+// merged online as in combine_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void combine_cascade_kernel(const AttnParams p) {
+    constexpr int NQ = D / 4;
+    constexpr int SG = 256 / NQ;
+    constexpr int CH = 8;
+    constexpr int RS = partial_stride<D>();
+    __shared__ float s_m[SG], s_l[SG];
+    __shared__ f32x4 s_o[SG][NQ];
+    const int t = threadIdx.x;
+    const int qc = t % NQ, sg = t / NQ;
+    const int g = blockIdx.x % p.R;
+    const int kh = (blockIdx.x / p.R) % p.H;
+    const int b = blockIdx.x / (p.R * p.H);
+    const int npages = (p.seq_lens[b] + 15) >> 4;
+    const int n_suf = min(p.n_splits, (max(0, npages - p.page_lo) + p.split_pages - 1) / p.split_pages);
+    const float* pre = p.pre_partials + ((size_t)kh * p.pre_splits * p.pre_R + (size_t)b * p.R + g) * RS;
+    const size_t pre_step = (size_t)p.pre_R * RS;
+    const float* suf = p.partials + (((size_t)b * p.H + kh) * p.n_splits * p.R + g) * RS;
+    const size_t suf_step = (size_t)p.R * RS;
+    const int total = p.pre_eff + p.n_splits;
+    float M = kNegInf, Ls = 0.0f;
+    f32x4 O = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u0 = sg; u0 < total; u0 += SG * CH) {
+        float m[CH], l[CH];
+        f32x4 o[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int u = u0 + c * SG;
+            if (u < total) {
+                const float* rec = u < p.pre_eff ? pre + (size_t)u * pre_step : suf + (size_t)(u - p.pre_eff) * suf_step;
+                m[c] = rec[0];
+                l[c] = rec[1];
+                o[c] = *((const f32x4*)(rec + 4) + qc);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int u = u0 + c * SG;
+            if (u >= total || (u >= p.pre_eff && u - p.pre_eff >= n_suf)) {
+                m[c] = kNegInf;
+                l[c] = 0.0f;
+                o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        float Mn = M;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, m[c]);
+        if (Mn != kNegInf) {
+            const float a = exp2_fast(M - Mn);
+            O *= a;
+            Ls *= a;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const float wgt = exp2_fast(m[c] - Mn);
+                O += o[c] * wgt;
+                Ls += l[c] * wgt;
+            }
+            M = Mn;
+        }
+    }
+    if (qc == 0) {
+        s_m[sg] = M;
+        s_l[sg] = Ls;
+    }
+    s_o[sg][qc] = O;
+    __syncthreads();
+    if (t < NQ) {
+        float Mg = kNegInf;
+#pragma unroll
+        for (int k = 0; k < SG; ++k) Mg = fmaxf(Mg, s_m[k]);
+        const float ref = (Mg == kNegInf) ? 0.0f : Mg;
+        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+        float Lt = 0.0f;
+#pragma unroll
+        for (int k = 0; k < SG; ++k) {
+            const float wgt = exp2_fast(s_m[k] - ref);
+            sum += s_o[k][t] * wgt;
+            Lt += s_l[k] * wgt;
+        }
+        const float inv = (Lt > 0.0f) ? 1.0f / Lt : 0.0f;
+        *((f32x4*)(p.out + out_index(p, b, kh, g, D)) + t) = sum * inv;
     }
 }
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_mfma_kernel(const AttnParams 
     if (!work_item(p, w)) return;
     const int r0 = w.rchunk * RW;
     if (w.pbeg >= w.pend) {
-        if (w.split == 0) write_zero_rows<D>(p, w, r0, RW);
+        if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, r0, RW);
         return;
     }
     const int n16 = lane & 15;             // MFMA column (query row) / output dimension

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
     WorkItem w;
     if (!work_item(p, w)) return;
     if (w.pbeg >= w.pend) {
-        if (w.split == 0) write_zero_rows<D>(p, w, 0, R);
+        if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, 0, R);
         return;
     }
     const int n16 = lane & 15;
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
     if (!work_item(p, w)) return;
     const int r0 = w.rchunk * RW;
     if (w.pbeg >= w.pend) {
-        if (w.split == 0) write_zero_rows<D>(p, w, r0, RW);
+        if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, r0, RW);
         return;
     }
     const int n16 = lane & 15;
@@ -821,7 +821,7 @@ LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
     if (rows_per_wg == 16 * RB_ && waves == W_ && stages == S_) return &launch_rows_t<D, RB_, W_, S_, QBF16>;
     Q8K4V_CASE(1, 2, 2) Q8K4V_CASE(1, 2, 3) Q8K4V_CASE(1, 4, 2) Q8K4V_CASE(1, 4, 3)
     Q8K4V_CASE(2, 2, 2) Q8K4V_CASE(2, 2, 3) Q8K4V_CASE(2, 4, 2) Q8K4V_CASE(2, 4, 3)
-    Q8K4V_CASE(1, 8, 2) Q8K4V_CASE(2, 8, 2)
+    Q8K4V_CASE(1, 8, 2) Q8K4V_CASE(2, 8, 2) Q8K4V_CASE(1, 8, 3) Q8K4V_CASE(2, 8, 3)
 #undef Q8K4V_CASE
     return nullptr;
 }

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_valu_kernel(const AttnParams 
     const int kh = w.kh, b = w.b, L = w.L, pend = w.pend;
     const int G = p.G, W = p.W;
     if (w.pbeg >= pend) {
-        if (w.split == 0) write_zero_rows<D>(p, w, 0, R);
+        if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, 0, R);
         return;
     }
 
@@ -396,6 +396,13 @@ hipError_t launch_combine_t(const AttnParams& kp, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_combine_cascade_t(const AttnParams& kp, hipStream_t stream) {
+    const int blocks = kp.n_seqs * kp.H * kp.R;
+    hipLaunchKernelGGL((combine_cascade_kernel<D>), dim3(blocks), dim3(256), 0, stream, kp);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int32_t launch_valu(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
@@ -416,6 +423,13 @@ int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipS
     (void)rows_per_wg;
     const hipError_t e = head_dim == 128 ? launch_combine_t<128>(kp, stream) : launch_combine_t<64>(kp, stream);
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    return Q8K4V_OK;
+}
+
+// Combine of the shared-prefix cascade (prefix-pass and suffix-pass records).
+int32_t launch_combine_cascade(const AttnParams& kp, int head_dim, hipStream_t stream) {
+    const hipError_t e = head_dim == 128 ? launch_combine_cascade_t<128>(kp, stream) : launch_combine_cascade_t<64>(kp, stream);
+    if (e != hipSuccess) return hip_fail(e, "cascade combine kernel launch");
     return Q8K4V_OK;
 }
 

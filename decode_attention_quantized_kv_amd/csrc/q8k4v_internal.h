@@ -74,6 +74,17 @@ size_t plan_workspace(const Plan& p);
 int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
+// Shared-prefix cascade: the prefix pass (row-block kernel over the shared
+// pages, every session's rows), the suffix pass (the decode plan past the
+// prefix) and their partial areas, prefix first.
+struct CascadePlan {
+    Plan pre, suf;
+};
+constexpr int32_t kMaxPrefixRows = 4096;
+int32_t make_cascade_plan(const AttnArgs& a, int32_t n_prefix_pages, const q8k4v_config* cfg, CascadePlan* cp);
+int32_t launch_cascade(const AttnArgs& a, int32_t n_prefix_pages, const CascadePlan& cp, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 // Tuned table (installed by tune_select), per current device and shape;
 // n_draft 1 is the decode unit.  lookup returns true and fills cfg on a match.
 bool tuned_lookup(int32_t n_draft, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

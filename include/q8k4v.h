@@ -87,8 +87,8 @@ typedef struct q8k4v_config {
     int32_t tile_pages;      /* pages staged in LDS per wave per step: 1, 2 or 4 (the
                                 MFMA variants fix it: 4 for 2, 2 for 3 and 4)          */
     int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup (variants 4 and 5: 2, 4
-                                or 8; variant 5 with 8 waves needs 2 stages). Default
-                                4, or 8 for variant 5 above 16 rows per kv head      */
+                                or 8). Default 4, or 8 for variant 5 above 16 rows
+                                per kv head                                           */
     int32_t fused_combine;   /* 1: the last workgroup of a (sequence, kv head) merges
                                 the splits (needs a zeroed workspace counter area);
                                 0: a separate combine kernel                           */
@@ -175,6 +175,48 @@ int32_t attn_decode_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
                           const int32_t *page_table, int32_t max_pages, float softmax_scale,
                           const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * attn_decode_prefix_q8k4v -- decode of sessions that share a prompt prefix
+ * (blog.123qwe.co.kr/?p=3927, section 5: concurrent sessions over one cached
+ * prefix).  Same result as attn_decode_q8k4v on the same arguments, computed
+ * as a cascade so that the shared pages are read once for all sessions:
+ *  1. prefix pass: the first n_prefix_pages logical pages, taken from row 0
+ *     of page_table, against the query rows of every session at once (a
+ *     dense (n_seqs * group) x D query block per kv head on the 16x16 MFMA
+ *     row-block kernel), split-K partials per session row;
+ *  2. suffix pass: each session's pages from n_prefix_pages on, split-K as
+ *     in attn_decode_q8k4v;
+ *  3. combine: per (session, q head), the log-sum-exp merge of both partial
+ *     sets, normalised into out.
+ *
+ *   n_prefix_pages  host: leading logical pages shared by every session.
+ *                   Precondition (device data, not checked): for every b,
+ *                   page_table[b][i] == page_table[0][i] for i < n_prefix_pages
+ *                   and seq_lens[b] >= 16 * n_prefix_pages; if violated the
+ *                   output is undefined (with page ids in range no access
+ *                   leaves the pools).
+ *                   0 runs attn_decode_q8k4v.
+ *   cfg             applies to the suffix pass; the prefix pass uses the
+ *                   row-block kernel's defaults
+ *   workspace       at least q8k4v_prefix_workspace_bytes(...) bytes
+ * Other arguments as attn_decode_q8k4v.  Errors as attn_decode_q8k4v, plus
+ * EINVAL for n_prefix_pages outside 0 .. min(max_pages, max_seq_len / 16)
+ * and EUNSUPPORTED for more than 4096 query rows per kv head.
+ */
+int32_t attn_decode_prefix_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dtype,
+                                 float *out, int32_t n_seqs, int32_t num_q_heads,
+                                 const int32_t *seq_lens, int32_t max_seq_len,
+                                 const int32_t *page_table, int32_t max_pages,
+                                 int32_t n_prefix_pages, float softmax_scale,
+                                 const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Workspace (bytes) of attn_decode_prefix_q8k4v: both passes' split
+ * partials (no counters, nothing to zero).  Returns 0 on invalid shapes. */
+size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t max_seq_len, int32_t n_prefix_pages,
+                                    const q8k4v_config *cfg);
 
 /*
  * attn_verify_q8k4v -- n_draft draft queries per sequence, causal among the

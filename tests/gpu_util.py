@@ -43,3 +43,15 @@ def run_attention(w, cache, cfg=None, q=None, seq_lens=None, max_seq_len=None):
         out = q8.attn_decode_q8k4v(cache, q, lens, msl, pt, w.softmax_scale, cfg=cfg)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
+
+
+def run_prefix(w, cache, n_prefix_pages, cfg=None, max_seq_len=None):
+    """attn_decode_prefix_q8k4v on a decode workload whose sequences share
+    their first n_prefix_pages pages."""
+    q = to_dev(w.q, w.dtype)
+    lens = to_dev(w.seq_lens)
+    pt = to_dev(w.page_table)
+    msl = int(max(w.seq_lens)) if max_seq_len is None else max_seq_len
+    out = q8.attn_decode_prefix_q8k4v(cache, q, lens, msl, pt, n_prefix_pages, w.softmax_scale, cfg=cfg)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)

@@ -28,9 +28,10 @@ def lib():
     return q8.load_library()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select"):
+    for n in ("kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select",
+              "attn_decode_prefix_q8k4v", "q8k4v_prefix_workspace_bytes"):
         assert n in names
 
 
@@ -97,6 +98,32 @@ def test_workspace_size_follows_the_plan(lib):
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(split_pages=4096, variant=4)) > 0
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(waves_per_wg=3)) == 0  # invalid config
     assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(variant=2)) == 0  # 1 row: no block MFMA
+
+
+def test_prefix_cascade_validation_and_workspace(lib):
+    """The shared-prefix entry point validates its page count on the host
+    (before any launch) and sizes its workspace as prefix + suffix partials."""
+    d = q8.CacheDesc(8192, 4, 128, 16, 1, 1, 1, 1)
+
+    def casc(n_pref, msl=65536, mp=4096, n=16, hq=32, ws=None, wsb=0):
+        return lib.attn_decode_prefix_q8k4v(C.byref(d), 1, 1, 1, n, hq, 1, msl, 1, mp, n_pref, 0.1, None, ws, wsb,
+                                            None)
+    assert casc(-1) == -1
+    assert casc(4097) == -1                     # more pages than the page table holds
+    assert casc(100, msl=1000) == -1            # prefix longer than max_seq_len
+    assert casc(2048, hq=30) == -1              # bad head counts are still caught
+    assert casc(2048, n=1024) == -2             # 1024 sessions x 8 rows: prefix block too large
+    rc = casc(2048)                             # workspace missing
+    assert rc == -3 and b"workspace" in lib.q8k4v_last_error()
+    full = q8.workspace_bytes(16, 32, 4, 128, 65536)
+    pre = q8.prefix_workspace_bytes(16, 32, 4, 128, 65536, 2048)
+    assert pre > 0
+    assert q8.prefix_workspace_bytes(16, 32, 4, 128, 65536, 0) == full
+    assert q8.prefix_workspace_bytes(16, 32, 4, 128, 1000, 100) == 0
+    # the prefix partials alone: 4 kv heads x splits x 128 rows x 132 floats
+    assert pre >= 4 * 128 * 132 * 4
+    # one session, whole context shared: still a valid cascade
+    assert q8.prefix_workspace_bytes(1, 8, 8, 64, 4096, 256) > 0
 
 
 def test_tuner_rejects_bad_requests(lib):

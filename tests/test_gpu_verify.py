@@ -47,7 +47,7 @@ def test_verify_rows_equal_decodes_on_gpu():
 
 
 @pytest.mark.parametrize("cfg", [dict(waves_per_wg=2), dict(waves_per_wg=4), dict(fused_combine=1),
-                                 dict(split_pages=2), dict(wgs_per_cu=6), dict(variant=5, stages=3),
+                                 dict(split_pages=2), dict(wgs_per_cu=6), dict(variant=5, stages=3), dict(variant=5, waves_per_wg=8, stages=3),
                                  dict(variant=5, waves_per_wg=2, stages=2, fused_combine=1),
                                  dict(variant=3), dict(variant=3, waves_per_wg=1), dict(variant=3, fused_combine=1)],
                          ids=str)
