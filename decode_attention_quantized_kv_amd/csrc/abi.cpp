@@ -451,10 +451,22 @@ size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv
     return plan_workspace(p);
 }
 
+// Suffix-pass configuration of the cascade: the caller's, else the decode
+// defaults with more, shorter splits (ragged suffixes balance better).
+static const q8k4v_config* cascade_config(const q8k4v_config* cfg, int32_t num_q_heads, int32_t num_kv_heads,
+                                          q8k4v_config* dflt) {
+    if (cfg || num_kv_heads <= 0) return cfg;
+    *dflt = default_config(std::max(1, num_q_heads / num_kv_heads));
+    dflt->wgs_per_cu = kCascadeSuffixWgsPerCu;
+    return dflt;
+}
+
 size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_seq_len, int32_t n_prefix_pages, const q8k4v_config* cfg) {
     if (n_prefix_pages == 0)
         return q8k4v_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 0, cfg);
+    q8k4v_config dflt;
+    cfg = cascade_config(cfg, num_q_heads, num_kv_heads, &dflt);
     q8k4v_cache fake;
     const AttnArgs a = shape_args(&fake, n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 1);
     CascadePlan cp;
@@ -503,6 +515,8 @@ int32_t attn_decode_prefix_q8k4v(const q8k4v_cache* cache, const void* q, int32_
                                page_table, max_pages, softmax_scale, cfg, workspace, workspace_bytes, stream);
     AttnArgs a{cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens, max_seq_len,
                page_table, max_pages, softmax_scale};
+    q8k4v_config dflt;
+    cfg = cascade_config(cfg, num_q_heads, cache ? cache->num_kv_heads : 0, &dflt);
     CascadePlan cp;
     int32_t rc = make_plan(a, cfg, &cp.suf);        // validates the shape as a decode launch
     if (rc == Q8K4V_OK) rc = make_cascade_plan(a, n_prefix_pages, cfg, &cp);

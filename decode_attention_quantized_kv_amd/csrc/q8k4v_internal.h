@@ -81,6 +81,7 @@ struct CascadePlan {
     Plan pre, suf;
 };
 constexpr int32_t kMaxPrefixRows = 4096;
+constexpr int32_t kCascadeSuffixWgsPerCu = 4;   // suffix pass, when the caller gives no config
 int32_t make_cascade_plan(const AttnArgs& a, int32_t n_prefix_pages, const q8k4v_config* cfg, CascadePlan* cp);
 int32_t launch_cascade(const AttnArgs& a, int32_t n_prefix_pages, const CascadePlan& cp, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);

@@ -197,8 +197,9 @@ int32_t attn_decode_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
  *                   output is undefined (with page ids in range no access
  *                   leaves the pools).
  *                   0 runs attn_decode_q8k4v.
- *   cfg             applies to the suffix pass; the prefix pass uses the
- *                   row-block kernel's defaults
+ *   cfg             applies to the suffix pass (NULL: the decode defaults
+ *                   with wgs_per_cu 4); the prefix pass uses the row-block
+ *                   kernel's defaults
  *   workspace       at least q8k4v_prefix_workspace_bytes(...) bytes
  * Other arguments as attn_decode_q8k4v.  Errors as attn_decode_q8k4v, plus
  * EINVAL for n_prefix_pages outside 0 .. min(max_pages, max_seq_len / 16)
