@@ -25,6 +25,9 @@ int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool q
 int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
 int32_t launch_combine_cascade(const AttnParams& kp, int head_dim, hipStream_t stream);
+bool cascade_fusable(const Plan& pre, const Plan& suf);
+int32_t launch_cascade_fused(const AttnParams& pre, const AttnParams& suf, int head_dim, bool qbf16, int rows,
+                             hipStream_t stream);
 
 namespace {
 thread_local std::string g_last_error;
@@ -300,12 +303,16 @@ int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace, s
 // ---- shared-prefix cascade ------------------------------------------------
 // Sessions whose first n_prefix_pages logical pages are the same physical
 // pages (a shared prompt prefix, blog.123qwe.co.kr/?p=3927, section 5) are
-// decoded in three launches: a prefix pass of the row-block kernel over one
-// virtual sequence -- the shared pages, read once for all sessions -- whose
-// query rows are every session's rows (session j as "draft" j, no causal
-// edge inside the prefix); a suffix pass, the plain decode plan over each
-// session's pages from n_prefix_pages on; and a combine that merges both
-// record sets per (session, q head) by log-sum-exp.
+// decoded in two passes and a combine: a prefix pass of the row-block kernel
+// over one virtual sequence -- the shared pages, read once for all sessions
+// -- whose query rows are every session's rows (session j as "draft" j, no
+// causal edge inside the prefix); a suffix pass, the plain decode plan over
+// each session's pages from n_prefix_pages on; and a combine that merges both
+// record sets per (session, q head) by log-sum-exp.  When the suffix plan is
+// the four-wave, two-stage replicated-row kernel and the prefix block has more
+// than 16 rows, both passes run in one launch (the prefix pass then takes
+// four waves too): the compute-bound prefix workgroups and the memory-bound
+// suffix workgroups share the CUs.
 int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config* cfg, CascadePlan* cp) {
     if (n_pref < 1 || n_pref > a.max_pages || (int64_t)n_pref * Q8K4V_PAGE_SIZE > a.max_seq_len)
         return fail(Q8K4V_EINVAL, "attention: n_prefix_pages must be in 1 .. min(max_pages, max_seq_len / 16)");
@@ -331,7 +338,11 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     pp.kernel = kRows;
     pp.mfma = 1;
     pp.tile_pages = 2;
-    pp.waves = rows > 16 ? 8 : 4;
+    // 8 waves for a large prefix block on its own; 4 when it shares the
+    // launch with a four-wave, two-stage replicated-row suffix pass
+    const bool fuse = rows > 16 && sp.kernel == kDec2 && (sp.rows == 4 || sp.rows == 8) && sp.waves == 4 &&
+                      sp.stages == 2;
+    pp.waves = (rows > 16 && !fuse) ? 8 : 4;
     pp.stages = 2;
     pp.rows_per_wg = rows > 16 ? 32 : 16;
     pp.row_chunks = (pp.rows + pp.rows_per_wg - 1) / pp.rows_per_wg;
@@ -369,8 +380,6 @@ int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp,
     pre.cascade = 1;
     pre.direct = 0;
     pre.fused = 0;
-    int32_t rc = launch_rows(pre, cp.pre, D, bf, stream);
-    if (rc != Q8K4V_OK) return rc;
 
     AttnParams suf = launch_params(a, cp.suf, suf_part);
     suf.partials = suf_part;
@@ -378,8 +387,17 @@ int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp,
     suf.cascade = 1;
     suf.direct = 0;
     suf.fused = 0;
-    rc = launch_kernel(suf, cp.suf, D, bf, stream);
-    if (rc != Q8K4V_OK) return rc;
+
+    int32_t rc;
+    if (cascade_fusable(cp.pre, cp.suf)) {
+        rc = launch_cascade_fused(pre, suf, D, bf, cp.suf.rows, stream);
+        if (rc != Q8K4V_OK) return rc;
+    } else {
+        rc = launch_rows(pre, cp.pre, D, bf, stream);
+        if (rc != Q8K4V_OK) return rc;
+        rc = launch_kernel(suf, cp.suf, D, bf, stream);
+        if (rc != Q8K4V_OK) return rc;
+    }
 
     suf.pre_partials = pre_part;
     suf.pre_splits = cp.pre.n_splits;

@@ -65,9 +65,9 @@ struct WorkItem {
 // the XCDs, starting at a different XCD per sequence, so a ragged batch
 // loads the XCDs evenly.  Otherwise XCD x takes the x-th eighth of the items
 // in order.
-Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w) {
+Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w, int bid) {
     const int C = p.H * p.row_chunks;          // items per (sequence, split)
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int x = bid & 7, j = bid >> 3;
     int inner;
     if ((p.n_splits & 7) == 0) {
         const int S8 = p.n_splits >> 3;        // splits per sequence and XCD
@@ -97,6 +97,7 @@ Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w) {
     w.pend = min(w.npages, w.pbeg + p.split_pages);
     return true;
 }
+Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w) { return work_item(p, w, (int)blockIdx.x); }
 
 Q8K4V_DEV size_t out_index(const AttnParams& p, int b, int kh, int r, int D) {
     const int j = r / p.G, g = r % p.G;

@@ -83,8 +83,16 @@ Q8K4V_DEV void v_word_to_f16(uint32_t x, uint32_t out[4]) {
     out[3] = as_u32(__builtin_elementwise_fma(as_h2(nib_to_f16(y, 0x64706470u, 0x64806480u)), inv16, off16));
 }
 
+// Bytes of one 2-page tile in LDS: key codes, value codes, key scales,
+// value scales of both pages (6464 B at D = 128).
+template <int D>
+constexpr int ring_stage_bytes() { return 2 * (16 * D + 8 * D + 32 + 32 * (D / 32)); }
+
+// The kernel bodies take their tile ring (WAVES x STAGES stages, in LDS) and
+// their block index as arguments so that one launch can run two of them
+// (the shared-prefix cascade's fused pass).
 template <int D, int R, int WAVES, int STAGES, bool QBF16>
-__global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
+Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;                      // pages per tile
     constexpr int KB = 16 * D, VB = 8 * D;     // key / value code bytes per page
     constexpr int NG = D / 32;                 // value groups
@@ -100,14 +108,14 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
     static_assert(16 % R == 0, "R must divide 16");
     static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
     static_assert(R * D * 4 <= STAGES * STAGE, "the merge buffer reuses the tile ring");
+    static_assert(STAGE == ring_stage_bytes<D>(), "tile layout");
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES][STAGES][STAGE];
     __shared__ float s_ml[WAVES][R][2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WorkItem w;
-    if (!work_item(p, w)) return;
+    if (!work_item(p, w, bid)) return;
     if (w.pbeg >= w.pend) {
         if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, 0, R);
         return;
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
         if (lane < TP * nt) my_id = p.page_table[(size_t)w.b * p.max_pages + min(pg, pend - 1)];
     }
 
-    uint8_t* const stage0 = &s_stage[wave][0][0];
+    uint8_t* const stage0 = smem + wave * STAGES * STAGE;
     const uint32_t lds0 = lds_addr(stage0);
     uint32_t kdma_off[KI];                     // key rows swizzled: chunk c of row t at t*CPR + (c ^ t%CPR)
 #pragma unroll
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
         s_ml[wave][n16][1] = l_tot;
     }
     __syncthreads();           // every wave is done with its ring: reuse it for O
-    float* s_o = (float*)&s_stage[0][0][0];   // [WAVES][R][D]
+    float* s_o = (float*)smem;   // [WAVES][R][D]
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
         const int g = dt / 2;
@@ -385,7 +393,13 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
                 s_o[(wave * R + idx % R) * D + 16 * dt + n16] = acc[dt][i];
         }
     }
-    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, &s_stage[0][0][0], (int)sizeof(s_stage));
+    finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, smem, WAVES * STAGES * STAGE);
+}
+
+template <int D, int R, int WAVES, int STAGES, bool QBF16>
+__global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D>()];
+    dec2_body<D, R, WAVES, STAGES, QBF16>(p, s_stage, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,10 +414,10 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
 //    fp16 multiply; products of p <= 1 and an fp16 scale cannot overflow);
 //  * O tile dt (value group dt/2) on v_mfma_f32_16x16x32_f16 with the exact
 //    fp16 value codes: lane (n, q) holds rows 16 rb + 4q + i, dim 16 dt + n.
-// The waves' outputs are merged in wave order through one LDS buffer.
+// The waves' outputs are merged in a fixed two-round tree through LDS.
 // ---------------------------------------------------------------------------
 template <int D, int RB, int WAVES, int STAGES, bool QBF16>
-__global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
+Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;
     constexpr int KB = 16 * D, VB = 8 * D;
     constexpr int NG = D / 32;
@@ -421,14 +435,14 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
     constexpr int SOS = D + 4;                 // merge-buffer row stride: lane groups 4 rows apart
                                                // land 16 banks apart
     static_assert(RW * SOS * 4 <= WAVES * STAGES * STAGE, "the merge buffer reuses the tile ring");
+    static_assert(STAGE == ring_stage_bytes<D>(), "tile layout");
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES][STAGES][STAGE];
     __shared__ float s_ml[WAVES][RW][2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     WorkItem w;
-    if (!work_item(p, w)) return;
+    if (!work_item(p, w, bid)) return;
     const int r0 = w.rchunk * RW;
     if (w.pbeg >= w.pend) {
         if (w.split == 0 && !p.cascade) write_zero_rows<D>(p, w, r0, RW);
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
         const int pg = w.pbeg + TP * (wave + WAVES * (lane >> 1)) + (lane & 1);
         if (lane < TP * nt) my_id = p.page_table[(size_t)w.b * p.max_pages + min(pg, pend - 1)];
     }
-    uint8_t* const stage0 = &s_stage[wave][0][0];
+    uint8_t* const stage0 = smem + wave * STAGES * STAGE;
     const uint32_t lds0 = lds_addr(stage0);
     uint32_t kdma_off[KI];
 #pragma unroll
@@ -737,7 +751,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
     constexpr int NB = WAVES / 2;
     constexpr int BUF = RW * SOS;
     static_assert(NB * BUF * 4 <= WAVES * STAGES * STAGE, "merge buffers reuse the tile ring");
-    float* s_o = (float*)&s_stage[0][0][0];
+    float* s_o = (float*)smem;
 #pragma unroll
     for (int round = 0; round < 2; ++round) {
         const bool mine = round == 0 ? wave >= NB : wave < NB;
@@ -771,7 +785,26 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
         __syncthreads();
     }
     emit_rows<D, RW, SOS>(p, w, r0, s_M, s_L, s_o);
-    fused_tail<D, RW>(p, w, r0, &s_stage[0][0][0], (int)sizeof(s_stage));
+    fused_tail<D, RW>(p, w, r0, smem, WAVES * STAGES * STAGE);
+}
+
+template <int D, int RB, int WAVES, int STAGES, bool QBF16>
+__global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D>()];
+    rows_body<D, RB, WAVES, STAGES, QBF16>(p, s_stage, (int)blockIdx.x);
+}
+
+// Fused pass of the shared-prefix cascade: blocks [0, pre_blocks) run the
+// prefix pass (row-block body, 32 rows per workgroup, over the shared pages),
+// the rest the suffix pass (replicated-row body, one session's G rows), with
+// one tile ring per workgroup.  Both are four-wave, two-stage rings, so a
+// compute-bound prefix workgroup and memory-bound suffix workgroups share
+// each CU.  pre_blocks is a multiple of 8, which keeps every block's XCD.
+template <int D, int R, bool QBF16>
+__global__ __launch_bounds__(256) void attn_cascade_kernel(const AttnParams pre, const AttnParams suf, int pre_blocks) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D>()];
+    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16>(pre, s_stage, (int)blockIdx.x);
+    else dec2_body<D, R, 4, 2, QBF16>(suf, s_stage, (int)blockIdx.x - pre_blocks);
 }
 
 template <int D, int RB, int WAVES, int STAGES, bool QBF16>
@@ -826,7 +859,43 @@ LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
     return nullptr;
 }
 
+template <int D, int R, bool QBF16>
+hipError_t launch_cascade_t(const AttnParams& pre, const AttnParams& suf, hipStream_t stream) {
+    const int pre_total = pre.n_seqs * pre.H * pre.n_splits * pre.row_chunks;
+    const int pre_blocks = 8 * ((pre_total + 7) / 8);
+    const int suf_total = suf.n_seqs * suf.H * suf.n_splits * suf.row_chunks;
+    const int suf_blocks = 8 * ((suf_total + 7) / 8);
+    hipLaunchKernelGGL((attn_cascade_kernel<D, R, QBF16>), dim3(pre_blocks + suf_blocks), dim3(256), 0, stream,
+                       pre, suf, pre_blocks);
+    return hipGetLastError();
+}
+
+template <int D, bool QBF16>
+hipError_t pick_cascade(int rows, const AttnParams& pre, const AttnParams& suf, hipStream_t stream) {
+    switch (rows) {
+        case 4: return launch_cascade_t<D, 4, QBF16>(pre, suf, stream);
+        case 8: return launch_cascade_t<D, 8, QBF16>(pre, suf, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+// One launch of both cascade passes (prefix plan: 32-row blocks, 4 waves, 2
+// stages; suffix plan: replicated rows, 4 or 8 rows, 4 waves, 2 stages).
+bool cascade_fusable(const Plan& pre, const Plan& suf) {
+    return pre.kernel == kRows && pre.rows_per_wg == 32 && pre.waves == 4 && pre.stages == 2 &&
+           suf.kernel == kDec2 && (suf.rows == 4 || suf.rows == 8) && suf.waves == 4 && suf.stages == 2;
+}
+
+int32_t launch_cascade_fused(const AttnParams& pre, const AttnParams& suf, int head_dim, bool qbf16, int rows,
+                             hipStream_t stream) {
+    hipError_t e;
+    if (head_dim == 128) e = qbf16 ? pick_cascade<128, true>(rows, pre, suf, stream) : pick_cascade<128, false>(rows, pre, suf, stream);
+    else e = qbf16 ? pick_cascade<64, true>(rows, pre, suf, stream) : pick_cascade<64, false>(rows, pre, suf, stream);
+    if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
+    return Q8K4V_OK;
+}
 
 int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
     LaunchFn fn = nullptr;
