@@ -348,7 +348,10 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     pp.row_chunks = (pp.rows + pp.rows_per_wg - 1) / pp.rows_per_wg;
     const int32_t unit = pp.tile_pages * pp.waves;
     const int64_t per = (int64_t)H * pp.row_chunks;
-    const int64_t splits = std::max<int64_t>(1, (device_cu_count() + per - 1) / per);
+    // one prefix workgroup per CU on its own; one per two CUs in the fused
+    // launch, which leaves room for the suffix workgroups (measured)
+    const int64_t target = fuse ? device_cu_count() / 2 : device_cu_count();
+    const int64_t splits = std::max<int64_t>(1, (target + per - 1) / per);
     int32_t spp = round_up((int32_t)((n_pref + splits - 1) / splits), unit);
     spp = std::min(std::max(spp, unit), 64 * pp.waves);
     pp.split_pages = spp;
