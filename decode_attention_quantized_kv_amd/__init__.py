@@ -59,7 +59,7 @@ class TuneRequest(C.Structure):
                 ("ref_cache", C.POINTER(CacheDesc)), ("ref_q", C.c_void_p), ("ref_q_verify", C.c_void_p),
                 ("ref_page_table", C.c_void_p), ("ref_len", C.c_int32), ("ref_max_pages", C.c_int32),
                 ("ref_out", C.c_void_p), ("ref_out_verify", C.c_void_p), ("ref_tol", C.c_float),
-                ("softmax_scale", C.c_float)]
+                ("softmax_scale", C.c_float), ("record_path", C.c_char_p)]
 
 
 _lib = None
@@ -278,11 +278,13 @@ def attn_verify_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_t
 def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int = 8,
                 ctx_small: int = 4096, ctx_large: int = 65536, budget_ms: int = 60000,
                 mem_cap_bytes: int = 0, seed: int = 0, install: bool = False, max_candidates: int = 0,
-                ref=None, report_cap: int = 1 << 20):
+                ref=None, report_cap: int = 1 << 20, record_path: Optional[str] = None):
     """Runs the on-device tuner.  ``ref`` (optional) is a dict with keys
     ``cache`` (PagedKVCache), ``q``, ``q_verify``, ``page_table`` (device),
     ``length``, ``out``, ``out_verify`` (host float32 numpy) and ``tol``.
-    Returns (decode Config, verify Config, report dict)."""
+    ``record_path`` (optional): file of stored choices, reused for the same
+    device identity and request shape.  Returns (decode Config, verify
+    Config, report dict)."""
     lib = load_library()
     req = TuneRequest()
     req.num_q_heads, req.num_kv_heads, req.head_dim, req.n_draft = num_q_heads, num_kv_heads, head_dim, n_draft
@@ -303,6 +305,8 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
         req.ref_out = out.ctypes.data
         req.ref_out_verify = outv.ctypes.data
         req.ref_tol = float(ref["tol"])
+    if record_path is not None:
+        req.record_path = os.fsencode(record_path)
     table = (Config * 2)()
     buf = C.create_string_buffer(report_cap)
     rc = lib.tune_select(C.byref(req), table, buf, report_cap)

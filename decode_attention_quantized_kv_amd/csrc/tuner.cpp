@@ -14,11 +14,23 @@
 // for the small context, over disjoint page sets) whose total exceeds four
 // times the 256 MiB last-level cache, so every launch streams from HBM.
 //
-// Order: the default, then the structural variants (which kernel), then a
-// refinement of the launch shape (waves per workgroup, workgroups per CU,
-// fused combine) around the best structural choice.  A candidate that is not
-// fully measured and checked before the deadline is "unknown" and is never
-// admitted.  Admission: on each of the unit's two shapes, the candidate's
+// Order: each unit's default first; then one candidate at a time from the
+// unit with the earliest virtual completion time
+//     (effort + price) / (share x opportunity)
+// (section 3 of the same page): effort = wall time already spent on the unit,
+// price = wall time of its last measurement, share = the unit's part of the
+// default service time, opportunity = the fraction of its generated
+// candidates still unmeasured.  Within a unit, the structural variants (which
+// kernel) come first, then a refinement of the launch shape (stages, waves
+// per workgroup, workgroups per CU, fused combine) around the best structural
+// choice.  A candidate that is not fully measured and checked before the
+// deadline is "unknown" and is never admitted.
+//
+// Records: with a record path, the choice is stored per device identity
+// (architecture, device name and CU count, HIP runtime and driver versions,
+// library build) and request shape; a later call with the same identity and
+// shape uses the stored choice without measuring, and a changed identity
+// (new driver, toolchain or library) searches again.  Admission: on each of the unit's two shapes, the candidate's
 // output may differ from the default configuration's output by at most
 // alpha = 8 times the storage-resolution noise -- the change of the default
 // output when every stored code moves by one quantisation step -- and, when
@@ -30,6 +42,8 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <fstream>
+#include <sstream>
 #include <string>
 #include <vector>
 
@@ -132,6 +146,20 @@ struct Cand {
     double dev[2] = {0, 0};        // max |out - default out| per shape
     double ref_dev = -1;
     double cost = 0;
+    int seq = -1;                  // position in the measurement order (both units)
+    double vt[2] = {-1, -1};       // virtual completion times of the units when it was picked
+};
+
+// Search state of one unit: measured candidates (default first), the queue
+// of generated but unmeasured ones, and the accounting of the search order.
+struct UnitSearch {
+    std::vector<Cand> cands;
+    std::vector<Cand> queue;       // front first
+    size_t best_i = 0;
+    bool active = false;           // default admitted: the unit is searched
+    bool refined = false;          // refinement queue generated
+    int generated = 0;             // non-default candidates generated so far
+    double effort_ms = 0, price_ms = 0;
 };
 
 struct Arena {
@@ -182,7 +210,8 @@ class Tuner {
     int32_t time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us);
     int32_t output(const q8k4v_config* cfg, const Shape& s, int copy, std::vector<float>* host);
     int32_t ref_output(const q8k4v_config* cfg, bool verify, std::vector<float>* host);
-    void tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, bool* qualified);
+    void start_unit(int unit, UnitSearch* u);
+    void refine_queue(int unit, UnitSearch* u);
     void measure(int unit, Cand* c);
 
     const q8k4v_tune_request& req_;
@@ -209,6 +238,7 @@ class Tuner {
     double def_t_[2][2] = {{0, 0}, {0, 0}};
     std::vector<float> ref_host_[2];
     std::string setup_note_;
+    int seq_ = 0;                        // measurement order over both units
     std::string summary_, error_;
 
   public:
@@ -460,14 +490,14 @@ void Tuner::measure(int unit, Cand* c) {
     c->verdict = "admitted";
 }
 
-void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, bool* qualified) {
+// Measures the unit's default (its times normalise the cost, its outputs are
+// the gate) and queues the structural variants.  Nothing is searched when the
+// default itself is unmeasured, invalid or fails the caller's references.
+void Tuner::start_unit(int unit, UnitSearch* u) {
     const int rows = rows_of(unit);
     const bool paged16 = rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16;
     const q8k4v_config dflt = default_config(rows);
-    *chosen = dflt;
-    *qualified = false;
-
-    // the default: its times normalise the cost; its outputs are the gate
+    const auto t0 = Clock::now();
     Cand d;
     d.cfg = dflt;
     d.stage = "default";
@@ -496,23 +526,13 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
         d.verdict = (d.ref_dev < 0 || d.ref_dev <= req_.ref_tol) ? "admitted" : "rejected";
         if (d.verdict == "rejected") d.why = "reference deviation " + fmt(d.ref_dev) + " > ref_tol";
     }
-    cands->push_back(d);
-    // nothing is searched when the default itself is unmeasured, invalid or
-    // fails the caller's references: its times and outputs are the yardstick
-    if (d.verdict != "admitted") return;
-    size_t best_i = cands->size() - 1;
-    const int limit = req_.max_candidates > 0 ? req_.max_candidates : (1 << 20);
-    auto consider = [&](const q8k4v_config& c, const char* stage) {
-        for (const auto& e : *cands)
-            if (same_cfg(e.cfg, c)) return;
-        if ((int)cands->size() >= limit) return;
-        Cand x;
-        x.cfg = c;
-        x.stage = stage;
-        measure(unit, &x);
-        cands->push_back(x);
-        if (x.verdict == "admitted" && x.cost < (*cands)[best_i].cost) best_i = cands->size() - 1;
-    };
+    d.seq = seq_++;
+    u->cands.push_back(d);
+    u->best_i = 0;
+    u->price_ms = std::chrono::duration<double, std::milli>(Clock::now() - t0).count();
+    u->effort_ms = u->price_ms;
+    u->active = d.verdict == "admitted";
+    if (!u->active) return;
     // structural variants: which kernel runs the unit (each with its own
     // launch-shape defaults)
     std::vector<int> variants;
@@ -522,14 +542,29 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
     }
     variants.push_back(3);
     for (int v : variants) {
-        q8k4v_config c = dflt;
-        c.variant = v;
-        c.wgs_per_cu = c.waves_per_wg = c.stages = 0;
-        consider(c, "structural");
+        Cand c;
+        c.cfg = dflt;
+        c.cfg.variant = v;
+        c.cfg.wgs_per_cu = c.cfg.waves_per_wg = c.cfg.stages = 0;
+        c.stage = "structural";
+        u->queue.push_back(c);
     }
-    // refinement of the launch shape around the best structural choice
-    const q8k4v_config base = (*cands)[best_i].cfg;
+    u->generated = (int)u->queue.size();
+}
+
+// Queues the refinement of the launch shape around the best candidate so far.
+void Tuner::refine_queue(int unit, UnitSearch* u) {
+    u->refined = true;
+    const bool paged16 = [&] { const int r = rows_of(unit); return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }();
+    const q8k4v_config base = u->cands[u->best_i].cfg;
     const bool base_paged = base.variant == 4 || (base.variant == 0 && paged16);
+    auto push = [&](const q8k4v_config& c) {
+        Cand x;
+        x.cfg = c;
+        x.stage = "refine";
+        u->queue.push_back(x);
+        ++u->generated;
+    };
     for (int fused : {0, 1}) {
         if (base_paged) {
             for (int stages : {3, 2})
@@ -541,7 +576,7 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
                         c.wgs_per_cu = wgs;
                         c.stages = stages;
                         c.fused_combine = fused;
-                        consider(c, "refine");
+                        push(c);
                     }
         } else {
             for (int waves : {2, 4, 1})
@@ -550,13 +585,84 @@ void Tuner::tune_unit(int unit, std::vector<Cand>* cands, q8k4v_config* chosen, 
                     c.waves_per_wg = waves;
                     c.wgs_per_cu = wgs;
                     c.fused_combine = fused;
-                    consider(c, "refine");
+                    push(c);
                 }
         }
     }
-    const Cand& b = (*cands)[best_i];
-    *chosen = b.cfg;
-    *qualified = b.verdict == "admitted";
+}
+
+// ---- records ----------------------------------------------------------------
+
+std::string device_identity() {
+    int dev = 0, rt = 0, drv = 0;
+    (void)hipGetDevice(&dev);
+    hipDeviceProp_t prop;
+    std::memset(&prop, 0, sizeof prop);
+    (void)hipGetDeviceProperties(&prop, dev);
+    (void)hipRuntimeGetVersion(&rt);
+    (void)hipDriverGetVersion(&drv);
+    std::string id = "arch=" + std::string(prop.gcnArchName) + ";device=" + std::string(prop.name) +
+                     ";cus=" + std::to_string(prop.multiProcessorCount) + ";hip_runtime=" + std::to_string(rt) +
+                     ";driver=" + std::to_string(drv) + ";library=" + q8k4v_version();
+    for (auto& ch : id)
+        if ((unsigned char)ch < 32 || ch == '"' || ch == '\\') ch = ' ';
+    return id;
+}
+
+std::string identity_hash(const std::string& id) {   // FNV-1a, 64 bits
+    uint64_t h = 1469598103934665603ull;
+    for (unsigned char ch : id) {
+        h ^= ch;
+        h *= 1099511628211ull;
+    }
+    char b[24];
+    std::snprintf(b, sizeof b, "%016llx", (unsigned long long)h);
+    return b;
+}
+
+constexpr const char* kRecordTag = "q8k4v-tune-record";
+
+// One stored choice: identity hash, request shape, unit, qualified flag and
+// the configuration, then a tab and the identity in words.
+struct Record {
+    std::string id_hash;
+    int n_draft = 0, hq = 0, hkv = 0, d = 0, ctx_small = 0, ctx_large = 0, unit = 0, qualified = 0;
+    q8k4v_config cfg{};
+};
+
+std::string record_line(const Record& r, const std::string& identity) {
+    char b[512];
+    std::snprintf(b, sizeof b, "%s 1 %s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d\t%s", kRecordTag,
+                  r.id_hash.c_str(), r.n_draft, r.hq, r.hkv, r.d, r.ctx_small, r.ctx_large, r.unit, r.qualified,
+                  r.cfg.variant, r.cfg.wgs_per_cu, r.cfg.split_pages, r.cfg.tile_pages, r.cfg.waves_per_wg,
+                  r.cfg.fused_combine, r.cfg.stages, identity.c_str());
+    return b;
+}
+
+bool parse_record(const std::string& line, Record* r) {
+    char tag[32] = {0}, hash[32] = {0};
+    int ver = 0;
+    int v[15];
+    const int n = std::sscanf(line.c_str(), "%31s %d %31s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", tag, &ver,
+                              hash, &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &v[7], &v[8], &v[9], &v[10],
+                              &v[11], &v[12], &v[13], &v[14]);
+    if (n != 18 || std::strcmp(tag, kRecordTag) != 0 || ver != 1 || std::strlen(hash) != 16) return false;
+    r->id_hash = hash;
+    r->n_draft = v[0]; r->hq = v[1]; r->hkv = v[2]; r->d = v[3]; r->ctx_small = v[4]; r->ctx_large = v[5];
+    r->unit = v[6]; r->qualified = v[7];
+    std::memset(&r->cfg, 0, sizeof r->cfg);
+    r->cfg.variant = v[8]; r->cfg.wgs_per_cu = v[9]; r->cfg.split_pages = v[10]; r->cfg.tile_pages = v[11];
+    r->cfg.waves_per_wg = v[12]; r->cfg.fused_combine = v[13]; r->cfg.stages = v[14];
+    r->cfg.qualified = r->qualified;
+    return r->unit == 0 || r->unit == 1;
+}
+
+std::vector<std::string> read_lines(const char* path) {
+    std::vector<std::string> lines;
+    std::ifstream f(path);
+    std::string line;
+    while (f && std::getline(f, line)) lines.push_back(line);
+    return lines;
 }
 
 int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
@@ -566,14 +672,103 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     w_ = req_.n_draft;
     out_table[0] = default_config(rows_of(0));
     out_table[1] = default_config(rows_of(1));
-    int32_t rc = setup(&why);
+    // stored choice for this device identity and request shape
+    const std::string identity = device_identity();
+    const std::string id_hash = identity_hash(identity);
+    const bool use_records = req_.record_path && req_.record_path[0];
+    auto matches = [&](const Record& r) {
+        return r.id_hash == id_hash && r.n_draft == req_.n_draft && r.hq == req_.num_q_heads &&
+               r.hkv == req_.num_kv_heads && r.d == req_.head_dim && r.ctx_small == req_.ctx_small &&
+               r.ctx_large == req_.ctx_large;
+    };
+    std::string record_action = "none";
+    bool stored[2] = {false, false};
+    Record rec[2];
+    if (use_records) {
+        for (const auto& line : read_lines(req_.record_path)) {
+            Record r;
+            if (parse_record(line, &r) && matches(r)) {
+                rec[r.unit] = r;
+                stored[r.unit] = true;
+            }
+        }
+    }
+    const bool from_records = stored[0] && stored[1];
     std::vector<Cand> cands[2];
     q8k4v_config chosen[2] = {out_table[0], out_table[1]};
     bool qual[2] = {false, false};
     bool searched = false;
-    if (rc == Q8K4V_OK && !expired()) {
+    int32_t rc = Q8K4V_OK;
+    if (from_records) {
+        record_action = "loaded";
+        for (int unit = 0; unit < 2; ++unit) {
+            chosen[unit] = rec[unit].cfg;
+            qual[unit] = rec[unit].qualified != 0;
+        }
+    } else {
+        rc = setup(&why);
+    }
+    if (!from_records && rc == Q8K4V_OK && !expired()) {
         searched = true;
-        for (int unit = 0; unit < 2; ++unit) tune_unit(unit, &cands[unit], &chosen[unit], &qual[unit]);
+        UnitSearch us[2];
+        for (int unit = 0; unit < 2; ++unit) start_unit(unit, &us[unit]);
+        const int limit = req_.max_candidates > 0 ? req_.max_candidates : (1 << 20);
+        for (;;) {
+            // the next candidate comes from the unit with the earliest virtual
+            // completion time; a unit whose structural variants are done gets
+            // its refinement queue first
+            double share_den = 0;
+            for (int unit = 0; unit < 2; ++unit)
+                if (us[unit].active) share_den += def_t_[unit][0] + def_t_[unit][1];
+            double vt[2] = {-1, -1};
+            int pick = -1;
+            for (int unit = 0; unit < 2; ++unit) {
+                UnitSearch& u = us[unit];
+                if (!u.active || (int)u.cands.size() >= limit) continue;
+                if (u.queue.empty() && !u.refined) refine_queue(unit, &u);
+                while (!u.queue.empty()) {    // already measured configurations are skipped
+                    bool dup = false;
+                    for (const auto& e : u.cands) dup = dup || same_cfg(e.cfg, u.queue.front().cfg);
+                    if (!dup) break;
+                    u.queue.erase(u.queue.begin());
+                }
+                if (u.queue.empty()) continue;
+                const double share = (def_t_[unit][0] + def_t_[unit][1]) / share_den;
+                const double opportunity = (double)u.queue.size() / std::max(1, u.generated);
+                vt[unit] = (u.effort_ms + u.price_ms) / (share * opportunity);
+                if (pick < 0 || vt[unit] < vt[pick]) pick = unit;
+            }
+            if (pick < 0) break;
+            UnitSearch& u = us[pick];
+            Cand x = u.queue.front();
+            u.queue.erase(u.queue.begin());
+            x.seq = seq_++;
+            x.vt[0] = vt[0];
+            x.vt[1] = vt[1];
+            const auto t0c = Clock::now();
+            measure(pick, &x);
+            const double dt = std::chrono::duration<double, std::milli>(Clock::now() - t0c).count();
+            u.effort_ms += dt;
+            u.price_ms = dt;
+            u.cands.push_back(x);
+            if (x.verdict == "admitted" && x.cost < u.cands[u.best_i].cost) u.best_i = u.cands.size() - 1;
+            if (x.verdict == "unknown") {   // the deadline passed: the rest stays unmeasured
+                for (int unit = 0; unit < 2; ++unit)
+                    for (auto& q : us[unit].queue) {
+                        q.verdict = "unknown";
+                        q.why = "deadline";
+                        us[unit].cands.push_back(q);
+                    }
+                break;
+            }
+        }
+        for (int unit = 0; unit < 2; ++unit) {
+            cands[unit] = us[unit].cands;
+            if (us[unit].cands.empty()) continue;
+            const Cand& b = us[unit].cands[us[unit].best_i];
+            chosen[unit] = b.cfg;
+            qual[unit] = b.verdict == "admitted";
+        }
     }
     for (int unit = 0; unit < 2; ++unit) {
         out_table[unit] = chosen[unit];
@@ -587,13 +782,41 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     if (req_.install && rc == Q8K4V_OK)
         for (int unit = 0; unit < 2; ++unit)
             if (qual[unit]) {
-                tuned_install(unit ? w_ : 1, hq_, h_, d_, out_table[unit]);
+                tuned_install(unit ? req_.n_draft : 1, req_.num_q_heads, req_.num_kv_heads, req_.head_dim,
+                              out_table[unit]);
                 install = true;
             }
+    // store a completed search (records of other identities and shapes stay)
+    if (use_records && searched) {
+        std::vector<std::string> keep;
+        for (const auto& line : read_lines(req_.record_path)) {
+            Record r;
+            if (parse_record(line, &r) && !matches(r)) keep.push_back(line);
+        }
+        for (int unit = 0; unit < 2; ++unit) {
+            Record r;
+            r.id_hash = id_hash;
+            r.n_draft = req_.n_draft; r.hq = req_.num_q_heads; r.hkv = req_.num_kv_heads; r.d = req_.head_dim;
+            r.ctx_small = req_.ctx_small; r.ctx_large = req_.ctx_large;
+            r.unit = unit;
+            r.qualified = qual[unit] ? 1 : 0;
+            r.cfg = out_table[unit];
+            keep.push_back(record_line(r, identity));
+        }
+        const std::string tmp = std::string(req_.record_path) + ".tmp";
+        bool ok;
+        {
+            std::ofstream f(tmp, std::ios::trunc);
+            for (const auto& line : keep) f << line << "\n";
+            ok = (bool)f;
+        }
+        ok = ok && std::rename(tmp.c_str(), req_.record_path) == 0;
+        record_action = ok ? "stored" : "unwritable";
+    }
     const double elapsed = std::chrono::duration<double, std::milli>(Clock::now() - t0).count();
 
     std::string j = "{";
-    j += "\"status\":\"" + std::string(searched ? "searched" : "defaults") + "\"";
+    j += "\"status\":\"" + std::string(from_records ? "stored" : (searched ? "searched" : "defaults")) + "\"";
     j += ",\"budget_ms\":" + std::to_string(std::min<int64_t>(req_.budget_ms, kMaxBudgetMs));
     j += ",\"elapsed_ms\":" + fmt(elapsed);
     j += ",\"alpha\":" + fmt(kAlpha);
@@ -603,6 +826,8 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
          fmt((double)n_copies_ * cache_bytes_ / (double)kLlcBytes) + ",\"launches_per_median\":" + std::to_string(reps_) + "}";
     if (!setup_note_.empty()) j += ",\"note\":\"" + setup_note_ + "\"";
     j += ",\"installed\":" + std::string(install ? "true" : "false");
+    j += ",\"identity\":\"" + identity + "\",\"identity_hash\":\"" + id_hash + "\"";
+    j += ",\"record\":\"" + record_action + "\"";
     j += ",\"units\":[";
     std::string cand_lists;
     for (int unit = 0; unit < 2; ++unit) {
@@ -635,7 +860,9 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             if (i) cand_lists += ",";
             cand_lists += "{\"stage\":\"" + c.stage + "\",\"cfg\":" + cfg_json(c.cfg) + ",\"verdict\":\"" + c.verdict +
                           "\",\"us\":[" + fmt(c.t[0]) + "," + fmt(c.t[1]) + "],\"dev\":[" + fmt(c.dev[0]) + "," +
-                          fmt(c.dev[1]) + "],\"cost\":" + fmt(c.cost);
+                          fmt(c.dev[1]) + "],\"cost\":" + fmt(c.cost) + ",\"seq\":" + std::to_string(c.seq) +
+                          ",\"vt\":[" + (c.vt[0] < 0 ? std::string("null") : fmt(c.vt[0])) + "," +
+                          (c.vt[1] < 0 ? std::string("null") : fmt(c.vt[1])) + "]";
             if (c.ref_dev >= 0) cand_lists += ",\"ref_dev\":" + fmt(c.ref_dev);
             if (!c.why.empty()) {
                 std::string w = c.why;

@@ -265,7 +265,14 @@ int32_t attn_verify_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
  * exceed alpha times the storage-resolution noise, i.e. the change of the
  * default output when every stored code is moved by one step; and, when the
  * caller supplies reference outputs, the deviation from them must not
- * exceed ref_tol.
+ * exceed ref_tol.  Search order (section 3): after both defaults, each next
+ * candidate comes from the unit with the earliest virtual completion time
+ * (effort + price) / (share x opportunity) -- wall time spent on the unit,
+ * wall time of its last measurement, its part of the default service time,
+ * the fraction of its generated candidates still unmeasured; within a unit,
+ * structurally different kernels before launch-shape refinement.  The JSON
+ * report lists every candidate with its verdict, measurement order ("seq")
+ * and both units' virtual times when it was picked ("vt").
  *
  *   req         host, see q8k4v_tune_request
  *   out_table   host [2]: [0] decode, [1] verify; `qualified` = 1 if a
@@ -297,6 +304,14 @@ typedef struct q8k4v_tune_request {
     const float *ref_out_verify;       /* host float32 [n_draft][num_q_heads][D]            */
     float ref_tol;                     /* absolute tolerance against the references         */
     float softmax_scale;               /* 0: 1/sqrt(D)                                      */
+    /* optional text file of stored choices (may be NULL): a call whose device
+       identity (architecture, device name and CU count, HIP runtime and driver
+       versions, library build) and request shape (n_draft, head counts,
+       head_dim, ctx_small, ctx_large) match stored records uses them without
+       measuring (report status "stored"); otherwise it searches and, when the
+       search ran, replaces the records of that identity and shape (other
+       records are kept) */
+    const char *record_path;
 } q8k4v_tune_request;
 
 int32_t tune_select(const q8k4v_tune_request *req, q8k4v_config *out_table,

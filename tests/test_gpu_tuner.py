@@ -128,3 +128,49 @@ def test_tuner_wrong_references_admit_nothing():
     for unit, cands in zip(rep["units"], rep["candidates"]):
         assert not unit["qualified"] and unit["admitted"] == 0
         assert cands[0]["verdict"] == "rejected"
+
+
+def test_tuner_search_order_follows_virtual_completion_time():
+    """After the defaults, each measured candidate came from the unit with the
+    earliest virtual completion time (effort + price) / (share x opportunity)
+    at that moment, and both units were searched."""
+    dcfg, vcfg, rep, _ = _tune(num_q_heads=32, num_kv_heads=8, head_dim=128, n_draft=8, ctx_small=1024,
+                               ctx_large=8192, budget_ms=6000, seed=7)
+    assert rep["status"] == "searched"
+    picked = sorted((c["seq"], u, c) for u, cands in enumerate(rep["candidates"]) for c in cands
+                    if c["stage"] != "default" and c["seq"] >= 0)
+    assert {u for _, u, _ in picked} == {0, 1}
+    assert [s for s, _, _ in picked] == list(range(2, 2 + len(picked)))   # the defaults are 0 and 1
+    for _, u, c in picked:
+        mine, other = c["vt"][u], c["vt"][1 - u]
+        assert mine is not None and mine > 0
+        assert other is None or mine <= other
+
+
+def test_tuner_records_reuse_and_identity_change(tmp_path):
+    path = str(tmp_path / "tune.rec")
+    kw = dict(num_q_heads=16, num_kv_heads=4, head_dim=128, n_draft=4, ctx_small=512, ctx_large=4096,
+              budget_ms=4000, seed=6, record_path=path)
+    d1, v1, rep1, _ = _tune(**kw)
+    assert rep1["status"] == "searched" and rep1["record"] == "stored"
+    ident = rep1["identity_hash"]
+    assert "arch=gfx950" in rep1["identity"] and "library=q8k4v" in rep1["identity"]
+    lines = open(path).read().splitlines()
+    assert len(lines) == 2 and all(l.split()[:3] == ["q8k4v-tune-record", "1", ident] for l in lines)
+    # the same identity and shape: the stored choice, nothing measured
+    d2, v2, rep2, wall = _tune(**kw)
+    assert rep2["status"] == "stored" and rep2["record"] == "loaded"
+    assert rep2["elapsed_ms"] < 500 and all(len(c) == 0 for c in rep2["candidates"])
+    assert d2.as_dict() == d1.as_dict() and v2.as_dict() == v1.as_dict()
+    # another shape keeps its own records beside the first ones
+    _tune(**{**kw, "n_draft": 2})
+    assert len(open(path).read().splitlines()) == 4
+    # another identity (a new driver, toolchain or library build) searches again
+    # and keeps the other identity's records; unreadable lines are dropped
+    text = open(path).read()
+    with open(path, "w") as f:
+        f.write(text.replace(ident, "0123456789abcdef") + "not a record\n")
+    d3, v3, rep3, _ = _tune(**kw)
+    assert rep3["status"] == "searched" and rep3["record"] == "stored"
+    hashes = [l.split()[2] for l in open(path).read().splitlines()]
+    assert hashes.count("0123456789abcdef") == 4 and hashes.count(ident) == 2 and len(hashes) == 6
