@@ -43,6 +43,25 @@ dimension D (64 or 128):
 
 Token p of a sequence lives at physical page ``page_table[p // 16]``,
 slot ``p % 16``.
+
+Affine variant (the blog's log line calls the codec affine, with 32-wide
+groups and an fp16 scale; it gives no formula, so these readings are taken)
+-------------------------------------------------------------------------
+* Unsigned codes with a zero point: keys 0..255 per (token, kv head), values
+  0..15 per (token, kv head, group of 32).
+* The block's range is widened to include zero: ``lo = min(min x, 0)``,
+  ``hi = max(max x, 0)`` -- zero is then exact and the scale is 0 only for
+  an all-zero block.
+* ``s = fp16((hi - lo) / qmax)``: fp32 subtraction, fp32 IEEE division, RNE
+  into fp16 (65504 on overflow).
+* zero point ``z = clamp(rint_half_even(-lo / s), 0, qmax)`` (fp32 division);
+  ``code = clamp(rint_half_even(x / s) + z, 0, qmax)``; ``s == 0`` gives
+  code 0 and zero point 0.
+* Dequantized value = ``(code - z) * s``.
+* Stored bytes: key codes ``code XOR 0x80`` (the code minus 128 as int8) in
+  ``k_codes``; key zero points ``z XOR 0x80`` in ``k_zeros [P][H][16]``
+  (int8); value nibbles hold the unsigned codes; value zero points one byte
+  per (token, group) in ``v_zeros [P][H][16][D/32]`` (uint8, 0..15).
 """
 
 from __future__ import annotations
@@ -122,6 +141,49 @@ def quantize_v(x: np.ndarray):
     return c.reshape(x.shape), s
 
 
+AFFINE_K_QMAX = 255
+AFFINE_V_QMAX = 15
+
+
+def quantize_block_affine(x: np.ndarray, qmax: int):
+    """Affine quantization of the last axis of ``x`` (float32), range widened
+    to include zero.  Returns (codes uint8 0..qmax with the shape of x, zero
+    points uint8 and scale bits uint16 with the shape of x without its last
+    axis)."""
+    x = np.asarray(x, dtype=np.float32)
+    lo = np.minimum(np.min(x, axis=-1), np.float32(0)).astype(np.float32)
+    hi = np.maximum(np.max(x, axis=-1), np.float32(0)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        rng = (hi - lo).astype(np.float32)          # fp32 subtraction
+    s16 = fp16_scale(rng, qmax)
+    s = s16.astype(np.float32)
+    safe = np.where(s == 0, np.float32(1), s).astype(np.float32)
+    z = np.clip(np.rint((-lo / safe).astype(np.float32)), 0, qmax)
+    z = np.where(s == 0, 0, z)
+    r = (x / safe[..., None]).astype(np.float32)    # fp32 IEEE division
+    c = np.clip(np.rint(r) + z[..., None], 0, qmax)
+    c = np.where(s[..., None] == 0, 0, c)
+    return c.astype(np.uint8), z.astype(np.uint8), s16.view(np.uint16)
+
+
+def quantize_k_affine(x: np.ndarray):
+    """Key rows ``[..., D]`` -> (codes uint8 ``[..., D]``, zero points uint8
+    ``[...]``, fp16 scale bits ``[...]``)."""
+    return quantize_block_affine(x, AFFINE_K_QMAX)
+
+
+def quantize_v_affine(x: np.ndarray):
+    """Value rows ``[..., D]`` -> (codes uint8 0..15 ``[..., D]``, zero points
+    ``[..., D/32]``, fp16 scale bits ``[..., D/32]``)."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    if d % V_GROUP:
+        raise ValueError("head_dim must be a multiple of 32")
+    g = x.reshape(x.shape[:-1] + (d // V_GROUP, V_GROUP))
+    c, z, s = quantize_block_affine(g, AFFINE_V_QMAX)
+    return c.reshape(x.shape), z, s
+
+
 def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
@@ -137,6 +199,18 @@ def dequantize_v(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
     return codes.astype(np.float64) * s
 
 
+def dequantize_k_affine(codes: np.ndarray, zeros: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """(code - z) * s for unsigned key codes ``[..., D]``."""
+    return (codes.astype(np.float64) - zeros.astype(np.float64)[..., None]) * fp16_bits_to_f64(scale_bits)[..., None]
+
+
+def dequantize_v_affine(codes: np.ndarray, zeros: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """(code - z) * s for unsigned value codes ``[..., D]``, per group of 32."""
+    z = np.repeat(zeros.astype(np.float64), V_GROUP, axis=-1)
+    s = np.repeat(fp16_bits_to_f64(scale_bits), V_GROUP, axis=-1)
+    return (codes.astype(np.float64) - z) * s
+
+
 # ---------------------------------------------------------------------------
 # paged cache
 # ---------------------------------------------------------------------------
@@ -144,20 +218,31 @@ def dequantize_v(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
 class PagedCache:
     """Four host arrays in the library's byte layout (see module docstring)."""
 
-    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int):
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, codec: str = "symmetric"):
         if head_dim not in (64, 128):
             raise ValueError("head_dim must be 64 or 128")
+        if codec not in ("symmetric", "affine"):
+            raise ValueError("codec must be 'symmetric' or 'affine'")
         P, H, D = num_pages, num_kv_heads, head_dim
         self.num_pages, self.num_kv_heads, self.head_dim = P, H, D
+        self.codec = codec
         self.k_codes = np.zeros((P, H, PAGE_SIZE, D), np.int8)
         self.k_scales = np.zeros((P, H, PAGE_SIZE), np.uint16)
         self.v_codes = np.zeros((P, H, D, PAGE_SIZE // 2), np.uint8)
         self.v_scales = np.zeros((P, H, PAGE_SIZE, D // V_GROUP), np.uint16)
+        if codec == "affine":
+            self.k_zeros = np.zeros((P, H, PAGE_SIZE), np.int8)
+            self.v_zeros = np.zeros((P, H, PAGE_SIZE, D // V_GROUP), np.uint8)
+
+    def _arrays(self):
+        extra = ("k_zeros", "v_zeros") if self.codec == "affine" else ()
+        return ("k_codes", "k_scales", "v_codes", "v_scales") + extra
 
     def copy(self) -> "PagedCache":
         c = PagedCache.__new__(PagedCache)
         c.num_pages, c.num_kv_heads, c.head_dim = self.num_pages, self.num_kv_heads, self.head_dim
-        for n in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        c.codec = self.codec
+        for n in self._arrays():
             setattr(c, n, getattr(self, n).copy())
         return c
 
@@ -169,9 +254,16 @@ class PagedCache:
         distinct."""
         pages = np.asarray(pages, np.int64)
         slots = np.asarray(slots, np.int64)
-        kc, ks = quantize_k(k_f32)          # [N][H][D], [N][H]
-        vc, vs = quantize_v(v_f32)          # [N][H][D], [N][H][D/32]
-        self.k_codes[pages, :, slots, :] = kc
+        if self.codec == "affine":
+            kc, kz, ks = quantize_k_affine(k_f32)       # [N][H][D], [N][H], [N][H]
+            vc, vz, vs = quantize_v_affine(v_f32)       # [N][H][D], [N][H][D/32] x2
+            self.k_codes[pages, :, slots, :] = (kc ^ np.uint8(0x80)).view(np.int8)
+            self.k_zeros[pages, :, slots] = (kz ^ np.uint8(0x80)).view(np.int8)
+            self.v_zeros[pages, :, slots, :] = vz
+        else:
+            kc, ks = quantize_k(k_f32)          # [N][H][D], [N][H]
+            vc, vs = quantize_v(v_f32)          # [N][H][D], [N][H][D/32]
+            self.k_codes[pages, :, slots, :] = kc
         self.k_scales[pages, :, slots] = ks
         self.v_scales[pages, :, slots, :] = vs
         nib = (vc.astype(np.int16) & 0xF).astype(np.uint8)   # [N][H][D]
@@ -193,14 +285,25 @@ class PagedCache:
         return self.k_codes[pages, h, slots, :]
 
     def v_codes_at(self, pages, slots, h):
+        """Value codes ``[N][D]``: two's complement nibbles (symmetric) or
+        unsigned 0..15 (affine)."""
         b = self.v_codes[pages, h, :, slots // 2]               # [N][D]
         n = np.where((slots % 2)[:, None] == 0, b & 0xF, b >> 4).astype(np.int16)
+        if self.codec == "affine":
+            return n.astype(np.uint8)
         return np.where(n >= 8, n - 16, n).astype(np.int8)
 
     def dequant_tokens(self, pages, slots, h):
         """fp64 K-hat and V-hat rows ``[N][D]`` of kv head h."""
         pages = np.asarray(pages, np.int64)
         slots = np.asarray(slots, np.int64)
+        if self.codec == "affine":
+            kc = (self.k_codes_at(pages, slots, h).view(np.uint8) ^ np.uint8(0x80))
+            kz = (self.k_zeros[pages, h, slots].view(np.uint8) ^ np.uint8(0x80))
+            kh = dequantize_k_affine(kc, kz, self.k_scales[pages, h, slots])
+            vh = dequantize_v_affine(self.v_codes_at(pages, slots, h), self.v_zeros[pages, h, slots, :],
+                                     self.v_scales[pages, h, slots, :])
+            return kh, vh
         kh = dequantize_k(self.k_codes_at(pages, slots, h), self.k_scales[pages, h, slots])
         vh = dequantize_v(self.v_codes_at(pages, slots, h), self.v_scales[pages, h, slots, :])
         return kh, vh

@@ -73,3 +73,30 @@ def codec_code(x: float, s: Fraction, qmax: int) -> int:
         return qmax if r > 0 else -qmax
     c = round_half_even_int(r)
     return max(-qmax, min(qmax, c))
+
+
+def affine_scale(lo: float, hi: float, qmax: int) -> Fraction:
+    """fp16 scale of the affine codec: RNE32(RNE32(hi - lo) / qmax) then RNE16,
+    overflow -> 65504 (lo <= 0 <= hi already widened)."""
+    rng = rne_f32(Fraction(hi) - Fraction(lo))
+    if rng == INF:
+        return Fraction(65504)
+    s16 = rne_f16(rne_f32(rng / qmax))
+    if s16 == INF:
+        return Fraction(65504)
+    return s16
+
+
+def affine_zero(lo: float, s: Fraction, qmax: int) -> int:
+    if s == 0:
+        return 0
+    return max(0, min(qmax, round_half_even_int(rne_f32(-Fraction(lo) / s))))
+
+
+def affine_code(x: float, s: Fraction, z: int, qmax: int) -> int:
+    if s == 0:
+        return 0
+    r = rne_f32(Fraction(x) / s)
+    if r in (INF, -INF):
+        return qmax if r > 0 else 0
+    return max(0, min(qmax, round_half_even_int(r) + z))
