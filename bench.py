@@ -32,9 +32,10 @@ HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 
 
-def cache_bytes_per_token_head(D: int) -> int:
+def cache_bytes_per_token_head(D: int, affine: bool = False) -> int:
     # key codes D + key scale 2 + value codes D/2 + value scales 2*D/32
-    return D + 2 + D // 2 + 2 * (D // 32)
+    # (+ key zero point 1 + value zero points D/32 with the affine codec)
+    return D + 2 + D // 2 + 2 * (D // 32) + ((1 + D // 32) if affine else 0)
 
 
 def parse():
@@ -51,6 +52,8 @@ def parse():
     ap.add_argument("--config", default="", help="JSON dict of launch config fields")
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention launches (profiling)")
     ap.add_argument("--contiguous-pages", action="store_true", help="identity page table (profiling)")
+    ap.add_argument("--codec", default="symmetric", choices=["symmetric", "affine"],
+                    help="cache codec (affine: unsigned codes with zero points)")
     ap.add_argument("--no-cascade", action="store_true",
                     help="shared-prefix workload: plain decode instead of the prefix cascade")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -86,7 +89,7 @@ def main() -> int:
         for a in w.appends:
             a.page_table = relabel(a.page_table)
     Hq, H, D = w.num_q_heads, w.num_kv_heads, w.head_dim
-    per_th = cache_bytes_per_token_head(D)
+    per_th = cache_bytes_per_token_head(D, args.codec == "affine")
     unique = w.unique_tokens()
     layer_bytes = w.num_pages * H * 16 * per_th
     layers = args.layers or max(2, -(-4 * LLC_BYTES // layer_bytes) + 1)
@@ -98,7 +101,7 @@ def main() -> int:
         return t.to(dev)
 
     bf = w.dtype == "bf16"
-    caches = [q8.PagedKVCache(w.num_pages, H, D) for _ in range(layers)]
+    caches = [q8.PagedKVCache(w.num_pages, H, D, codec=args.codec) for _ in range(layers)]
     batches = [(to_dev(a.k, bf), to_dev(a.v, bf), to_dev(a.cu_new), to_dev(a.start_pos), to_dev(a.page_table))
                for a in w.appends]
     for c in caches:
@@ -217,13 +220,13 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16 in, int8 K / int4 V codes, fp16 MACs, fp32 accumulate",
         "data": "synthetic (seeded N(0,1), 1% outlier channels x8, bf16), random page permutation",
-        "config": {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": H, "head_dim": D,
+        "config": {"workload": w.name, "codec": args.codec, "num_q_heads": Hq, "num_kv_heads": H, "head_dim": D,
                    "context": int(w.seq_lens.max()), "n_seqs": B, "n_draft": nd, "page_size": 16,
                    "rotating_layer_caches": layers, "layer_cache_bytes": layer_bytes,
                    "launch_config": tuned or (cfg.as_dict() if cfg else "default"),
                    "shared_prefix_pages": n_pref},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(w.name, nd),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(w.name if args.codec == "symmetric" else w.name + "_affine", nd),
                      "kernel": ("attn_decode_prefix_q8k4v launch (prefix-pass kernel + suffix-pass kernel"
                                 " + LSE combine kernel)" if n_pref else
                                 ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v")

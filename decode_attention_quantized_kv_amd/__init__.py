@@ -36,10 +36,14 @@ class Q8K4VError(RuntimeError):
         self.code = code
 
 
+CODEC_SYMMETRIC, CODEC_AFFINE = 0, 1
+
+
 class CacheDesc(C.Structure):
     _fields_ = [("num_pages", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("page_size", C.c_int32), ("k_codes", C.c_void_p), ("k_scales", C.c_void_p),
-                ("v_codes", C.c_void_p), ("v_scales", C.c_void_p)]
+                ("v_codes", C.c_void_p), ("v_scales", C.c_void_p), ("codec", C.c_int32),
+                ("k_zeros", C.c_void_p), ("v_zeros", C.c_void_p)]
 
 
 class Config(C.Structure):
@@ -145,32 +149,49 @@ def make_config(**kw) -> Config:
 
 
 class PagedKVCache:
-    """The four device pools of a paged k8v4 cache (torch tensors), in the
+    """The device pools of a paged k8v4 cache (torch tensors), in the
     library's layout:
 
     ``k_codes [P][H][16][D] int8``, ``k_scales [P][H][16]`` fp16 bits,
-    ``v_codes [P][H][D][8] uint8``, ``v_scales [P][H][16][D/32]`` fp16 bits."""
+    ``v_codes [P][H][D][8] uint8``, ``v_scales [P][H][16][D/32]`` fp16 bits;
+    with ``codec="affine"`` also ``k_zeros [P][H][16] int8`` and
+    ``v_zeros [P][H][16][D/32] uint8``."""
 
-    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda"):
+    def __init__(self, num_pages: int, num_kv_heads: int, head_dim: int, device="cuda", codec: str = "symmetric"):
         torch = _torch()
+        if codec not in ("symmetric", "affine"):
+            raise ValueError("codec must be 'symmetric' or 'affine'")
         P, H, D = num_pages, num_kv_heads, head_dim
         self.num_pages, self.num_kv_heads, self.head_dim = P, H, D
+        self.codec = codec
         self.k_codes = torch.zeros((P, H, PAGE_SIZE, D), dtype=torch.int8, device=device)
         self.k_scales = torch.zeros((P, H, PAGE_SIZE), dtype=torch.int16, device=device)
         self.v_codes = torch.zeros((P, H, D, PAGE_SIZE // 2), dtype=torch.uint8, device=device)
         self.v_scales = torch.zeros((P, H, PAGE_SIZE, D // 32), dtype=torch.int16, device=device)
+        self.k_zeros = self.v_zeros = None
+        if codec == "affine":
+            self.k_zeros = torch.zeros((P, H, PAGE_SIZE), dtype=torch.int8, device=device)
+            self.v_zeros = torch.zeros((P, H, PAGE_SIZE, D // 32), dtype=torch.uint8, device=device)
         self._desc = None
+
+    def pools(self):
+        extra = (self.k_zeros, self.v_zeros) if self.codec == "affine" else ()
+        return (self.k_codes, self.k_scales, self.v_codes, self.v_scales) + extra
 
     @property
     def desc(self) -> CacheDesc:
         if self._desc is None:
+            aff = self.codec == "affine"
             self._desc = CacheDesc(self.num_pages, self.num_kv_heads, self.head_dim, PAGE_SIZE,
                                    self.k_codes.data_ptr(), self.k_scales.data_ptr(),
-                                   self.v_codes.data_ptr(), self.v_scales.data_ptr())
+                                   self.v_codes.data_ptr(), self.v_scales.data_ptr(),
+                                   CODEC_AFFINE if aff else CODEC_SYMMETRIC,
+                                   self.k_zeros.data_ptr() if aff else None,
+                                   self.v_zeros.data_ptr() if aff else None)
         return self._desc
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+        return sum(t.numel() * t.element_size() for t in self.pools())
 
 
 def kv_quant_append(cache: PagedKVCache, k_new, v_new, cu_new, start_pos, page_table,

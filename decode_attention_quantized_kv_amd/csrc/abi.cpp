@@ -45,6 +45,8 @@ bool valid_cache(const q8k4v_cache* c, std::string* why) {
     if (c->page_size != Q8K4V_PAGE_SIZE) { *why = "page_size must be 16"; return false; }
     if (c->num_kv_heads < 1 || c->num_pages < 1) { *why = "num_kv_heads and num_pages must be >= 1"; return false; }
     if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales) { *why = "a cache pool pointer is NULL"; return false; }
+    if (c->codec != Q8K4V_CODEC_SYMMETRIC && c->codec != Q8K4V_CODEC_AFFINE) { *why = "codec must be 0 (symmetric) or 1 (affine)"; return false; }
+    if (c->codec == Q8K4V_CODEC_AFFINE && (!c->k_zeros || !c->v_zeros)) { *why = "an affine cache needs k_zeros and v_zeros"; return false; }
     return true;
 }
 
@@ -179,6 +181,8 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = kd.wgs_per_cu;
     if (cfg.stages <= 0) cfg.stages = kd.stages;
     if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = kd.waves_per_wg;
+    if (a.cache->codec == Q8K4V_CODEC_AFFINE && kernel != kDec2 && kernel != kRows)
+        return fail(Q8K4V_EUNSUPPORTED, "attention: an affine cache runs on variants 4 and 5 only");
     if (kernel == kDec2) {
         if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
             return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");
@@ -271,6 +275,9 @@ AttnParams launch_params(const AttnArgs& a, const Plan& plan, void* workspace) {
     kp.scale_log2 = a.softmax_scale * kLog2e;
     kp.direct = plan.n_splits == 1;
     kp.fused = plan.fused_combine;
+    kp.affine = c.codec == Q8K4V_CODEC_AFFINE;
+    kp.k_zeros = c.k_zeros;
+    kp.v_zeros = c.v_zeros;
     return kp;
 }
 
@@ -341,7 +348,7 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     // 8 waves for a large prefix block on its own; 4 when it shares the
     // launch with a four-wave, two-stage replicated-row suffix pass
     const bool fuse = rows > 16 && sp.kernel == kDec2 && (sp.rows == 4 || sp.rows == 8) && sp.waves == 4 &&
-                      sp.stages == 2;
+                      sp.stages == 2 && a.cache->codec == Q8K4V_CODEC_SYMMETRIC;
     pp.waves = (rows > 16 && !fuse) ? 8 : 4;
     pp.stages = 2;
     pp.rows_per_wg = rows > 16 ? 32 : 16;
@@ -392,7 +399,7 @@ int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp,
     suf.fused = 0;
 
     int32_t rc;
-    if (cascade_fusable(cp.pre, cp.suf)) {
+    if (cascade_fusable(cp.pre, cp.suf) && !pre.affine) {
         rc = launch_cascade_fused(pre, suf, D, bf, cp.suf.rows, stream);
         if (rc != Q8K4V_OK) return rc;
     } else {
@@ -446,6 +453,9 @@ static AttnArgs shape_args(q8k4v_cache* fake, int32_t n_seqs, int32_t num_q_head
     fake->k_scales = (uint16_t*)1;
     fake->v_codes = (uint8_t*)1;
     fake->v_scales = (uint16_t*)1;
+    fake->codec = Q8K4V_CODEC_SYMMETRIC;
+    fake->k_zeros = nullptr;
+    fake->v_zeros = nullptr;
     AttnArgs a{};
     a.cache = fake;
     a.q = (const void*)1;
@@ -488,15 +498,22 @@ size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t
         return q8k4v_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 0, cfg);
     q8k4v_config dflt;
     cfg = cascade_config(cfg, num_q_heads, num_kv_heads, &dflt);
-    q8k4v_cache fake;
-    const AttnArgs a = shape_args(&fake, n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 1);
-    CascadePlan cp;
-    std::string saved = g_last_error;
-    if (make_plan(a, cfg, &cp.suf) != Q8K4V_OK || make_cascade_plan(a, n_prefix_pages, cfg, &cp) != Q8K4V_OK) {
-        g_last_error = saved;
-        return 0;
+    // the prefix plan depends on the codec (only a symmetric cache fuses the
+    // two passes): the larger need of the codecs the configuration supports
+    size_t need = 0;
+    const std::string saved = g_last_error;
+    for (int32_t codec : {Q8K4V_CODEC_SYMMETRIC, Q8K4V_CODEC_AFFINE}) {
+        q8k4v_cache fake;
+        const AttnArgs a = shape_args(&fake, n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 1);
+        fake.codec = codec;
+        fake.k_zeros = (int8_t*)1;
+        fake.v_zeros = (uint8_t*)1;
+        CascadePlan cp;
+        if (make_plan(a, cfg, &cp.suf) == Q8K4V_OK && make_cascade_plan(a, n_prefix_pages, cfg, &cp) == Q8K4V_OK)
+            need = std::max(need, cp.pre.partial_bytes + cp.suf.partial_bytes);
     }
-    return cp.pre.partial_bytes + cp.suf.partial_bytes;
+    g_last_error = saved;
+    return need;
 }
 
 static int32_t attention_entry(const char* name, const q8k4v_cache* cache, const void* q, int32_t q_dtype,

@@ -11,6 +11,15 @@
 // codes and scales are bit-identical to any other implementation of the same
 // rule.
 //
+// Affine variant (the same page calls the codec affine): unsigned codes with
+// a zero point over the block's range widened to include zero,
+//   lo = min(min x, 0), hi = max(max x, 0), s = fp16_rne((hi - lo) / q),
+//   z = clamp(rint(-lo / s), 0, q), code = clamp(rint(x / s) + z, 0, q),
+// q = 255 for keys and 15 for values; s == 0 -> code and zero point 0.  Key
+// code and zero point bytes are stored XOR 0x80 (the value minus 128 as
+// int8, ready for the signed int8 MFMA); value nibbles and value zero points
+// are unsigned.
+//
 // One wavefront quantizes one (token, kv head): lane i holds dimensions
 // (D/64)*i .. (D/64)*i + D/64 - 1.  Value codes of two tokens share a byte
 // (slots 2j and 2j+1 of a page, dimension-major rows); when both tokens of a
@@ -41,6 +50,11 @@ Q8K4V_DEV float wave_max(float x, int lanes) {
     return x;
 }
 
+Q8K4V_DEV float wave_min(float x, int lanes) {
+    for (int m = 1; m < lanes; m <<= 1) x = fminf(x, __shfl_xor(x, m));
+    return x;
+}
+
 // fp16 scale of an absmax: IEEE fp32 division, RNE into fp16, saturating.
 Q8K4V_DEV _Float16 scale_of(float absmax, float qmax) {
     const float s32 = absmax / qmax;
@@ -56,10 +70,59 @@ Q8K4V_DEV int code_of(float x, float s, float qmax) {
     return (int)r;
 }
 
-template <int D, bool BF16>
+// Affine block parameters from the block's min and max (over the lanes that
+// hold it): fp16 scale and zero point.
+struct Affine {
+    _Float16 s16;
+    float s, z;
+};
+
+Q8K4V_DEV Affine affine_of(float mn, float mx, float qmax) {
+    const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
+    Affine a;
+    a.s16 = scale_of(hi - lo, qmax);
+    a.s = (float)a.s16;
+    a.z = (a.s == 0.0f) ? 0.0f : fminf(fmaxf(rintf(-lo / a.s), 0.0f), qmax);
+    return a;
+}
+
+Q8K4V_DEV int affine_code(float x, const Affine& a, float qmax) {
+    if (a.s == 0.0f) return 0;
+    return (int)fminf(fmaxf(rintf(x / a.s) + a.z, 0.0f), qmax);
+}
+
+// Value codes of one token for this lane's dimensions (nibble values: two's
+// complement when symmetric, unsigned when affine), with its group's scale
+// (and zero point) reduced over the LPG lanes of the group.
+template <int EPL, int LPG, bool AFF>
+Q8K4V_DEV void value_codes(const float (&x)[EPL], int (&c)[EPL], _Float16* s16, int* z) {
+    if (AFF) {
+        float mn = x[0], mx = x[0];
+#pragma unroll
+        for (int e = 1; e < EPL; ++e) { mn = fminf(mn, x[e]); mx = fmaxf(mx, x[e]); }
+        const Affine a = affine_of(wave_min(mn, LPG), wave_max(mx, LPG), 15.0f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) c[e] = affine_code(x[e], a, 15.0f);
+        *s16 = a.s16;
+        *z = (int)a.z;
+    } else {
+        float va = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) va = fmaxf(va, fabsf(x[e]));
+        va = wave_max(va, LPG);
+        *s16 = scale_of(va, 7.0f);
+        const float vs = (float)*s16;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) c[e] = code_of(x[e], vs, 7.0f);
+        *z = 0;
+    }
+}
+
+template <int D, bool BF16, bool AFF>
 __global__ __launch_bounds__(256) void append_kernel(
     int8_t* __restrict__ k_codes, uint16_t* __restrict__ k_scales,
-    uint8_t* __restrict__ v_codes, uint16_t* __restrict__ v_scales, int32_t H,
+    uint8_t* __restrict__ v_codes, uint16_t* __restrict__ v_scales,
+    int8_t* __restrict__ k_zeros, uint8_t* __restrict__ v_zeros, int32_t H,
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const int32_t* __restrict__ cu_new, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ page_table, int32_t max_pages, int32_t n_seqs,
@@ -90,31 +153,42 @@ __global__ __launch_bounds__(256) void append_kernel(
     // ---- keys ------------------------------------------------------------
     float kx[EPL];
     load_row<D, BF16>(k_new, (size_t)tok * H + h, lane, kx);
-    float ka = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) ka = fmaxf(ka, fabsf(kx[e]));
-    ka = wave_max(ka, 64);
-    const _Float16 ks16 = scale_of(ka, 127.0f);
-    const float ks = (float)ks16;
     int8_t* krow = k_codes + (blk * 16 + slot) * D + EPL * lane;
+    if (AFF) {
+        float mn = kx[0], mx = kx[0];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) krow[e] = (int8_t)code_of(kx[e], ks, 127.0f);
-    if (lane == 0) k_scales[blk * 16 + slot] = __builtin_bit_cast(uint16_t, ks16);
+        for (int e = 1; e < EPL; ++e) { mn = fminf(mn, kx[e]); mx = fmaxf(mx, kx[e]); }
+        const Affine a = affine_of(wave_min(mn, 64), wave_max(mx, 64), 255.0f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) krow[e] = (int8_t)(affine_code(kx[e], a, 255.0f) ^ 0x80);
+        if (lane == 0) {
+            k_scales[blk * 16 + slot] = __builtin_bit_cast(uint16_t, a.s16);
+            k_zeros[blk * 16 + slot] = (int8_t)((int)a.z ^ 0x80);
+        }
+    } else {
+        float ka = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ka = fmaxf(ka, fabsf(kx[e]));
+        ka = wave_max(ka, 64);
+        const _Float16 ks16 = scale_of(ka, 127.0f);
+        const float ks = (float)ks16;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) krow[e] = (int8_t)code_of(kx[e], ks, 127.0f);
+        if (lane == 0) k_scales[blk * 16 + slot] = __builtin_bit_cast(uint16_t, ks16);
+    }
 
     // ---- values ----------------------------------------------------------
     float vx[EPL];
     load_row<D, BF16>(v_new, (size_t)tok * H + h, lane, vx);
-    float va = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) va = fmaxf(va, fabsf(vx[e]));
-    va = wave_max(va, LPG);
-    const _Float16 vs16 = scale_of(va, 7.0f);
-    const float vs = (float)vs16;
-    const int g = lane / LPG;
-    if ((lane % LPG) == 0) v_scales[(blk * 16 + slot) * NG + g] = __builtin_bit_cast(uint16_t, vs16);
     int c[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) c[e] = code_of(vx[e], vs, 7.0f);
+    _Float16 vs16;
+    int vz;
+    value_codes<EPL, LPG, AFF>(vx, c, &vs16, &vz);
+    const int g = lane / LPG;
+    if ((lane % LPG) == 0) {
+        v_scales[(blk * 16 + slot) * NG + g] = __builtin_bit_cast(uint16_t, vs16);
+        if (AFF) v_zeros[(blk * 16 + slot) * NG + g] = (uint8_t)vz;
+    }
 
     const bool odd = slot & 1;
     const bool pair_new = odd ? (tok - 1 >= first) : (tok + 1 < last);
@@ -123,13 +197,9 @@ __global__ __launch_bounds__(256) void append_kernel(
     if (!odd && pair_new) {                       // quantize the odd neighbour's values
         float wx[EPL];
         load_row<D, BF16>(v_new, (size_t)(tok + 1) * H + h, lane, wx);
-        float wa = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) wa = fmaxf(wa, fabsf(wx[e]));
-        wa = wave_max(wa, LPG);
-        const float ws = (float)scale_of(wa, 7.0f);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) c2[e] = code_of(wx[e], ws, 7.0f);
+        _Float16 ws16;
+        int wz;
+        value_codes<EPL, LPG, AFF>(wx, c2, &ws16, &wz);
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -156,15 +226,18 @@ int32_t launch_append(const AppendArgs& a, hipStream_t stream) {
     const long blocks = (items + 3) / 4;
     if (blocks > 0x7FFFFFFFL) return fail(Q8K4V_EINVAL, "kv_quant_append: too many tokens in one call");
     dim3 grid((unsigned)blocks), block(256);
-#define Q8K4V_APPEND(DD, BB)                                                                   \
-    hipLaunchKernelGGL((append_kernel<DD, BB>), grid, block, 0, stream, c.k_codes, c.k_scales, \
-                       c.v_codes, c.v_scales, c.num_kv_heads, a.k_new, a.v_new, a.cu_new,     \
-                       a.start_pos, a.page_table, a.max_pages, a.n_seqs, a.total_new)
+#define Q8K4V_APPEND(DD, BB, AA)                                                                      \
+    hipLaunchKernelGGL((append_kernel<DD, BB, AA>), grid, block, 0, stream, c.k_codes, c.k_scales,    \
+                       c.v_codes, c.v_scales, c.k_zeros, c.v_zeros, c.num_kv_heads, a.k_new, a.v_new, \
+                       a.cu_new, a.start_pos, a.page_table, a.max_pages, a.n_seqs, a.total_new)
     const bool bf = a.dtype == Q8K4V_BF16;
+    const bool aff = c.codec == Q8K4V_CODEC_AFFINE;
     if (c.head_dim == 128) {
-        if (bf) Q8K4V_APPEND(128, true); else Q8K4V_APPEND(128, false);
+        if (aff) { if (bf) Q8K4V_APPEND(128, true, true); else Q8K4V_APPEND(128, false, true); }
+        else { if (bf) Q8K4V_APPEND(128, true, false); else Q8K4V_APPEND(128, false, false); }
     } else {
-        if (bf) Q8K4V_APPEND(64, true); else Q8K4V_APPEND(64, false);
+        if (aff) { if (bf) Q8K4V_APPEND(64, true, true); else Q8K4V_APPEND(64, false, true); }
+        else { if (bf) Q8K4V_APPEND(64, true, false); else Q8K4V_APPEND(64, false, false); }
     }
 #undef Q8K4V_APPEND
     const hipError_t e = hipGetLastError();

@@ -35,6 +35,11 @@ struct AttnParams {
     // pre_eff splits hold pages
     const float* __restrict__ pre_partials;
     int32_t pre_splits, pre_eff, pre_R;
+    // affine codec: per-token key zero points (z XOR 0x80) [P][H][16] and
+    // per-(token, group) value zero points [P][H][16][D/32]
+    int32_t affine;
+    const int8_t* __restrict__ k_zeros;
+    const uint8_t* __restrict__ v_zeros;
 };
 
 constexpr float kNegInf = -__builtin_inff();

@@ -84,31 +84,72 @@ Q8K4V_DEV void v_word_to_f16(uint32_t x, uint32_t out[4]) {
 }
 
 // Bytes of one 2-page tile in LDS: key codes, value codes, key scales,
-// value scales of both pages (6464 B at D = 128).
-template <int D>
-constexpr int ring_stage_bytes() { return 2 * (16 * D + 8 * D + 32 + 32 * (D / 32)); }
+// value scales of both pages (6464 B at D = 128), then with the affine codec
+// the key and value zero points (16 + 16 D/32 B per page; 6624 B at D = 128).
+template <int D, bool AFF = false>
+constexpr int ring_stage_bytes() { return 2 * (16 * D + 8 * D + 32 + 32 * (D / 32) + (AFF ? 16 + 16 * (D / 32) : 0)); }
+
+// sum over the four lane groups (lanes 16 and 32 apart), integers
+Q8K4V_DEV int xgroups_isum(int x) {
+    auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = (int)a[0] + (int)a[1];
+    auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return (int)b[0] + (int)b[1];
+}
+
+// Affine value codes: the word's unsigned nibbles become fp16 (code - z).
+// A nibble at bit 0 of a half is set into the fp16 1024 + code and the pair
+// zl = fp16 (-1024 - z_page0, -1024 - z_page1) is added; a nibble at bit 4
+// gives 1024 + 16 code, scaled by 1/16 and zh = fp16 (-64 - z) added.  Every
+// value is a small integer, so each step is exact.
+Q8K4V_DEV void v_word_to_f16_affine(uint32_t x, const uint32_t (&zl)[2], const uint32_t (&zh)[2], uint32_t out[4]) {
+    const uint32_t y = x >> 8;
+    const f16x2 inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    out[0] = as_u32(as_h2((x & 0x000F000Fu) | 0x64006400u) + as_h2(zl[0]));
+    out[1] = as_u32(__builtin_elementwise_fma(as_h2((x & 0x00F000F0u) | 0x64006400u), inv16, as_h2(zh[0])));
+    out[2] = as_u32(as_h2((y & 0x000F000Fu) | 0x64006400u) + as_h2(zl[1]));
+    out[3] = as_u32(__builtin_elementwise_fma(as_h2((y & 0x00F000F0u) | 0x64006400u), inv16, as_h2(zh[1])));
+}
+
+// Zero-point operands of value group g for the pairs of token 4q4 + j
+// (j = 0..3) of pages 0 and 1: vz0 / vz1 hold the lane's 4 NG zero-point
+// bytes of each page (token-major, byte j NG + g).  zl for j = 0, 2 (low
+// nibbles), zh for j = 1, 3 (high nibbles).
+template <int NG>
+Q8K4V_DEV void value_zero_pairs(const uint32_t* vz0, const uint32_t* vz1, int g, uint32_t (&zl)[2], uint32_t (&zh)[2]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int bi = j * NG + g, wi = bi >> 2, bb = bi & 3;
+        // byte bb of page 0 into bits 0..7, of page 1 into bits 16..23
+        const uint32_t zp = __builtin_amdgcn_perm(vz1[wi], vz0[wi], (uint32_t)bb | 0x0C00u | (uint32_t)(4 + bb) << 16 | 0x0C000000u);
+        if (j % 2 == 0) zl[j / 2] = zp | 0xE400E400u;            // -(1024 + z)
+        else zh[j / 2] = (zp << 4) | 0xD400D400u;                // -(64 + z)
+    }
+}
 
 // The kernel bodies take their tile ring (WAVES x STAGES stages, in LDS) and
 // their block index as arguments so that one launch can run two of them
 // (the shared-prefix cascade's fused pass).
-template <int D, int R, int WAVES, int STAGES, bool QBF16>
+template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;                      // pages per tile
     constexpr int KB = 16 * D, VB = 8 * D;     // key / value code bytes per page
     constexpr int NG = D / 32;                 // value groups
     constexpr int KSB = 32, VSB = 32 * NG;     // scale bytes per page
     constexpr int OFF_V = TP * KB, OFF_KS = OFF_V + TP * VB, OFF_VS = OFF_KS + TP * KSB;
-    constexpr int STAGE = OFF_VS + TP * VSB;   // 6464 B at D = 128
+    constexpr int KZB = 16, VZB = 16 * NG;     // affine zero-point bytes per page
+    constexpr int OFF_KZ = OFF_VS + TP * VSB, OFF_VZ = OFF_KZ + TP * KZB;
+    constexpr int STAGE = AFF ? OFF_VZ + TP * VZB : OFF_KZ;   // 6464 B at D = 128 (6624 affine)
     constexpr int CPR = D / 16;                // 16-byte chunks per key row
     constexpr int KS = D / 64;                 // 64-dimension k-steps of q.K
     constexpr int NDT = D / 16;                // 16-dimension output tiles
     constexpr int NA = (R * NG + 15) / 16;     // A tiles of (row, group) pairs
     constexpr int KI = KB / 1024;              // 1 KiB key copies per page
-    constexpr int IPT = TP * (KI + 3);         // copy instructions per tile
+    constexpr int IPT = TP * (KI + 3 + (AFF ? 2 : 0));   // copy instructions per tile
     static_assert(16 % R == 0, "R must divide 16");
     static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
     static_assert(R * D * 4 <= STAGES * STAGE, "the merge buffer reuses the tile ring");
-    static_assert(STAGE == ring_stage_bytes<D>(), "tile layout");
+    static_assert(STAGE == ring_stage_bytes<D, AFF>(), "tile layout");
 
     __shared__ float s_ml[WAVES][R][2];
 
@@ -159,6 +200,10 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
             }
             if (lane < 2) lds_dma16(p.k_scales + blk * 16, lane * 16, base + OFF_KS + u * KSB);
             if (lane < 2 * NG) lds_dma16(p.v_scales + blk * 16 * NG, lane * 16, base + OFF_VS + u * VSB);
+            if (AFF) {
+                if (lane < 1) lds_dma16(p.k_zeros + blk * 16, lane * 16, base + OFF_KZ + u * KZB);
+                if (lane < NG) lds_dma16(p.v_zeros + blk * 16 * NG, lane * 16, base + OFF_VZ + u * VZB);
+            }
         }
     };
     // ---- query row (n mod R) as the B operand: 15-bit fixed point
@@ -170,6 +215,7 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     u32x4 qhi[KS], qlo[KS];
     float coef;
     int lim;
+    int qsum = 0;                              // sum of the row's fixed-point Q (affine keys)
     {
         const size_t qoff = out_index(p, w.b, kh, row, D);
         float x[KS][16];
@@ -219,6 +265,10 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
                 uint32_t u[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) u[t] = fbits(__builtin_fmaf(x[ks][4 * c + t], sc, 12583040.0f));
+                if (AFF) {                     // Q = (int16) U - 128
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) qsum += (int)(int16_t)(u[t] & 0xFFFFu) - 128;
+                }
                 const uint32_t u01 = __builtin_amdgcn_perm(u[1], u[0], 0x05040100u);   // U0 | U1 << 16
                 const uint32_t u23 = __builtin_amdgcn_perm(u[3], u[2], 0x05040100u);
                 hw[c] = __builtin_amdgcn_perm(u23, u01, 0x07050301u);                 // byte 1 of U0..U3
@@ -229,6 +279,7 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
         }
         coef = p.scale_log2 * ldexpf(1.0f, e - 14);
         lim = w.L - p.W + 1 + row / p.G;
+        if (AFF) qsum = xgroups_isum(qsum);
     }
     const int lim_min = w.L - p.W + 1;         // every row sees the positions below this
 
@@ -276,6 +327,17 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     vsf[a][u][j] = h2f(*(const uint16_t*)(st + OFF_VS + u * VSB + ((4 * q4 + j) * NG + grp[a]) * 2));
+        // affine: key zero points of tokens 4q4 .. 4q4+3, value zero points
+        // of those tokens for every group (token-major bytes)
+        uint32_t kzw[TP] = {}, vz[TP][NG] = {};
+        if (AFF) {
+#pragma unroll
+            for (int u = 0; u < TP; ++u) {
+                kzw[u] = *(const uint32_t*)(st + OFF_KZ + u * KZB + 4 * q4);
+#pragma unroll
+                for (int wd = 0; wd < NG; ++wd) vz[u][wd] = *(const uint32_t*)(st + OFF_VZ + u * VZB + 4 * NG * q4 + 4 * wd);
+            }
+        }
         wait_lds_all();
 
         // ---- scores
@@ -298,7 +360,11 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
             const float kf[4] = {h2f((uint16_t)ksw[u].x), h2f((uint16_t)(ksw[u].x >> 16)), h2f((uint16_t)ksw[u].y),
                                  h2f((uint16_t)(ksw[u].y >> 16))};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[u][i] = (float)(256 * chi[u][i] + clo[u][i]) * (kf[i] * coef);
+            for (int i = 0; i < 4; ++i) {
+                int dot = 256 * chi[u][i] + clo[u][i];
+                if (AFF) dot -= (int)(int8_t)(kzw[u] >> (8 * i)) * qsum;   // q.(c - z) in fixed point
+                s[u][i] = (float)dot * (kf[i] * coef);
+            }
         }
         if ((pg0 + TP) * 16 > lim_min || pg0 + TP > pend) {      // tile reaches the causal edge / split end
 #pragma unroll
@@ -366,7 +432,13 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
         for (int dt = 0; dt < NDT; ++dt) {
             const int a = ((dt / 2) * R) / 16;
             uint32_t b[4];
-            v_word_to_f16(vx[dt], b);
+            if (AFF) {
+                uint32_t zl[2], zh[2];
+                value_zero_pairs<NG>(vz[0], vz[1], dt / 2, zl, zh);
+                v_word_to_f16_affine(vx[dt], zl, zh, b);
+            } else {
+                v_word_to_f16(vx[dt], b);
+            }
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, pa[a]),
                                                               __builtin_bit_cast(f16x8_t, u32x4{b[0], b[1], b[2], b[3]}),
                                                               acc[dt], 0, 0, 0);
@@ -396,10 +468,10 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     finish_workgroup<D, R, WAVES>(p, w, 0, s_ml, s_o, smem, WAVES * STAGES * STAGE);
 }
 
-template <int D, int R, int WAVES, int STAGES, bool QBF16>
+template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D>()];
-    dec2_body<D, R, WAVES, STAGES, QBF16>(p, s_stage, (int)blockIdx.x);
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
+    dec2_body<D, R, WAVES, STAGES, QBF16, AFF>(p, s_stage, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -416,26 +488,28 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
 //    fp16 value codes: lane (n, q) holds rows 16 rb + 4q + i, dim 16 dt + n.
 // The waves' outputs are merged in a fixed two-round tree through LDS.
 // ---------------------------------------------------------------------------
-template <int D, int RB, int WAVES, int STAGES, bool QBF16>
+template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;
     constexpr int KB = 16 * D, VB = 8 * D;
     constexpr int NG = D / 32;
     constexpr int KSB = 32, VSB = 32 * NG;
     constexpr int OFF_V = TP * KB, OFF_KS = OFF_V + TP * VB, OFF_VS = OFF_KS + TP * KSB;
-    constexpr int STAGE = OFF_VS + TP * VSB;
+    constexpr int KZB = 16, VZB = 16 * NG;     // affine zero-point bytes per page
+    constexpr int OFF_KZ = OFF_VS + TP * VSB, OFF_VZ = OFF_KZ + TP * KZB;
+    constexpr int STAGE = AFF ? OFF_VZ + TP * VZB : OFF_KZ;
     constexpr int CPR = D / 16;
     constexpr int KS = D / 64;
     constexpr int NDT = D / 16;
     constexpr int KI = KB / 1024;
-    constexpr int IPT = TP * (KI + 3);
+    constexpr int IPT = TP * (KI + 3 + (AFF ? 2 : 0));
     constexpr int RW = 16 * RB;                // rows per workgroup
     constexpr int NVW = NG / 2;                // 32-bit words of one token's value scales
     static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
     constexpr int SOS = D + 4;                 // merge-buffer row stride: lane groups 4 rows apart
                                                // land 16 banks apart
     static_assert(RW * SOS * 4 <= WAVES * STAGES * STAGE, "the merge buffer reuses the tile ring");
-    static_assert(STAGE == ring_stage_bytes<D>(), "tile layout");
+    static_assert(STAGE == ring_stage_bytes<D, AFF>(), "tile layout");
 
     __shared__ float s_ml[WAVES][RW][2];
 
@@ -483,6 +557,10 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
             }
             if (lane < 2) lds_dma16(p.k_scales + blk * 16, lane * 16, base + OFF_KS + u * KSB);
             if (lane < 2 * NG) lds_dma16(p.v_scales + blk * 16 * NG, lane * 16, base + OFF_VS + u * VSB);
+            if (AFF) {
+                if (lane < 1) lds_dma16(p.k_zeros + blk * 16, lane * 16, base + OFF_KZ + u * KZB);
+                if (lane < NG) lds_dma16(p.v_zeros + blk * 16 * NG, lane * 16, base + OFF_VZ + u * VZB);
+            }
         }
     };
 
@@ -491,6 +569,7 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     u32x4 qhi[RB][KS], qlo[RB][KS];
     float coef[RB];
     int lim[RB];
+    int qsum[RB];                              // sum of each row's fixed-point Q (affine keys)
     {
         float x[RB][KS][16];
 #pragma unroll
@@ -543,6 +622,7 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
             if (mx[rb] > 0.0f) (void)frexpf(mx[rb], &e);
             e = min(max(e, -110), 110);
             const float sc = ldexpf(1.0f, 14 - e);
+            int qs = 0;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 uint32_t hw[4], lw[4];
@@ -551,6 +631,10 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                     uint32_t u[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) u[t] = fbits(__builtin_fmaf(x[rb][ks][4 * c + t], sc, 12583040.0f));
+                    if (AFF) {                 // Q = (int16) U - 128
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) qs += (int)(int16_t)(u[t] & 0xFFFFu) - 128;
+                    }
                     const uint32_t u01 = __builtin_amdgcn_perm(u[1], u[0], 0x05040100u);
                     const uint32_t u23 = __builtin_amdgcn_perm(u[3], u[2], 0x05040100u);
                     hw[c] = __builtin_amdgcn_perm(u23, u01, 0x07050301u);
@@ -560,6 +644,7 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                 qlo[rb][ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
             }
             coef[rb] = p.scale_log2 * ldexpf(1.0f, e - 14);
+            qsum[rb] = AFF ? xgroups_isum(qs) : 0;
         }
     }
     const int lim_min = w.L - p.W + 1;
@@ -609,6 +694,17 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                 const u32x4 v = *(const u32x4*)(st + OFF_VS + u * VSB + 8 * NG * q4 + 16 * c);
                 vsr[u][4 * c] = v.x; vsr[u][4 * c + 1] = v.y; vsr[u][4 * c + 2] = v.z; vsr[u][4 * c + 3] = v.w;
             }
+        // affine: key zero points of tokens 4q4 .. 4q4+3, value zero points
+        // of those tokens for every group (token-major bytes)
+        uint32_t kzw[TP] = {}, vz[TP][NG] = {};
+        if (AFF) {
+#pragma unroll
+            for (int u = 0; u < TP; ++u) {
+                kzw[u] = *(const uint32_t*)(st + OFF_KZ + u * KZB + 4 * q4);
+#pragma unroll
+                for (int wd = 0; wd < NG; ++wd) vz[u][wd] = *(const uint32_t*)(st + OFF_VZ + u * VZB + 4 * NG * q4 + 4 * wd);
+            }
+        }
         wait_lds_all();
 
         // ---- scores
@@ -644,7 +740,11 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
             for (int u = 0; u < TP; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[u][i] = (float)(256 * chi[rb][u][i] + clo[rb][u][i]) * (kf[u][i] * coef[rb]);
+                for (int i = 0; i < 4; ++i) {
+                    int dot = 256 * chi[rb][u][i] + clo[rb][u][i];
+                    if (AFF) dot -= (int)(int8_t)(kzw[u] >> (8 * i)) * qsum[rb];   // q.(c - z) in fixed point
+                    s[u][i] = (float)dot * (kf[u][i] * coef[rb]);
+                }
             if (edge) {
 #pragma unroll
                 for (int u = 0; u < TP; ++u)
@@ -705,11 +805,14 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
             for (int rb = 0; rb < RB; ++rb)
                 pa[rb] = u32x4{as_u32(as_h2(pp[rb][0]) * as_h2(sp[0])), as_u32(as_h2(pp[rb][1]) * as_h2(sp[1])),
                                as_u32(as_h2(pp[rb][2]) * as_h2(sp[2])), as_u32(as_h2(pp[rb][3]) * as_h2(sp[3]))};
+            uint32_t zl[2] = {}, zh[2] = {};
+            if (AFF) value_zero_pairs<NG>(vz[0], vz[1], g, zl, zh);
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd) {
                 const int dt = 2 * g + dd;
                 uint32_t b[4];
-                v_word_to_f16(vx[dt], b);
+                if (AFF) v_word_to_f16_affine(vx[dt], zl, zh, b);
+                else v_word_to_f16(vx[dt], b);
                 const f16x8_t B = __builtin_bit_cast(f16x8_t, u32x4{b[0], b[1], b[2], b[3]});
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
@@ -788,10 +891,10 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     fused_tail<D, RW>(p, w, r0, smem, WAVES * STAGES * STAGE);
 }
 
-template <int D, int RB, int WAVES, int STAGES, bool QBF16>
+template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D>()];
-    rows_body<D, RB, WAVES, STAGES, QBF16>(p, s_stage, (int)blockIdx.x);
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
+    rows_body<D, RB, WAVES, STAGES, QBF16, AFF>(p, s_stage, (int)blockIdx.x);
 }
 
 // Fused pass of the shared-prefix cascade: blocks [0, pre_blocks) run the
@@ -803,55 +906,68 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
 template <int D, int R, bool QBF16>
 __global__ __launch_bounds__(256) void attn_cascade_kernel(const AttnParams pre, const AttnParams suf, int pre_blocks) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D>()];
-    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16>(pre, s_stage, (int)blockIdx.x);
-    else dec2_body<D, R, 4, 2, QBF16>(suf, s_stage, (int)blockIdx.x - pre_blocks);
+    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16, false>(pre, s_stage, (int)blockIdx.x);
+    else dec2_body<D, R, 4, 2, QBF16, false>(suf, s_stage, (int)blockIdx.x - pre_blocks);
 }
 
-template <int D, int RB, int WAVES, int STAGES, bool QBF16>
+template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 hipError_t launch_rows_t(const AttnParams& kp, hipStream_t stream) {
     const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
     const int blocks = 8 * ((total + 7) / 8);
-    hipLaunchKernelGGL((attn_rows_kernel<D, RB, WAVES, STAGES, QBF16>), dim3(blocks), dim3(64 * WAVES), 0, stream, kp);
+    hipLaunchKernelGGL((attn_rows_kernel<D, RB, WAVES, STAGES, QBF16, AFF>), dim3(blocks), dim3(64 * WAVES), 0, stream,
+                       kp);
     return hipGetLastError();
 }
 
-template <int D, int R, int WAVES, int STAGES, bool QBF16>
+template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 hipError_t launch_t(const AttnParams& kp, hipStream_t stream) {
     const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
     const int blocks = 8 * ((total + 7) / 8);
-    hipLaunchKernelGGL((attn_dec2_kernel<D, R, WAVES, STAGES, QBF16>), dim3(blocks), dim3(64 * WAVES), 0, stream, kp);
+    hipLaunchKernelGGL((attn_dec2_kernel<D, R, WAVES, STAGES, QBF16, AFF>), dim3(blocks), dim3(64 * WAVES), 0, stream,
+                       kp);
     return hipGetLastError();
 }
 
 using LaunchFn = hipError_t (*)(const AttnParams&, hipStream_t);
 
-template <int D, int R, bool QBF16>
+// Symmetric caches: every shape; affine caches: the two-stage 4- and 8-wave
+// shapes (the defaults), which bounds the number of kernel instances.
+template <int D, int R, bool QBF16, bool AFF>
 LaunchFn pick_shape(int waves, int stages) {
-    if (waves == 2 && stages == 2) return &launch_t<D, R, 2, 2, QBF16>;
-    if (waves == 2 && stages == 3) return &launch_t<D, R, 2, 3, QBF16>;
-    if (waves == 4 && stages == 2) return &launch_t<D, R, 4, 2, QBF16>;
-    if (waves == 4 && stages == 3) return &launch_t<D, R, 4, 3, QBF16>;
-    if (waves == 8 && stages == 2) return &launch_t<D, R, 8, 2, QBF16>;
-    if (waves == 8 && stages == 3) return &launch_t<D, R, 8, 3, QBF16>;
+    if (AFF) {
+        if (waves == 4 && stages == 2) return &launch_t<D, R, 4, 2, QBF16, AFF>;
+        if (waves == 8 && stages == 2) return &launch_t<D, R, 8, 2, QBF16, AFF>;
+        return nullptr;
+    }
+    if (waves == 2 && stages == 2) return &launch_t<D, R, 2, 2, QBF16, AFF>;
+    if (waves == 2 && stages == 3) return &launch_t<D, R, 2, 3, QBF16, AFF>;
+    if (waves == 4 && stages == 2) return &launch_t<D, R, 4, 2, QBF16, AFF>;
+    if (waves == 4 && stages == 3) return &launch_t<D, R, 4, 3, QBF16, AFF>;
+    if (waves == 8 && stages == 2) return &launch_t<D, R, 8, 2, QBF16, AFF>;
+    if (waves == 8 && stages == 3) return &launch_t<D, R, 8, 3, QBF16, AFF>;
     return nullptr;
 }
 
-template <int D, bool QBF16>
+template <int D, bool QBF16, bool AFF>
 LaunchFn pick(int rows, int waves, int stages) {
     switch (rows) {
-        case 1: return pick_shape<D, 1, QBF16>(waves, stages);
-        case 2: return pick_shape<D, 2, QBF16>(waves, stages);
-        case 4: return pick_shape<D, 4, QBF16>(waves, stages);
-        case 8: return pick_shape<D, 8, QBF16>(waves, stages);
-        case 16: return pick_shape<D, 16, QBF16>(waves, stages);
+        case 1: return pick_shape<D, 1, QBF16, AFF>(waves, stages);
+        case 2: return pick_shape<D, 2, QBF16, AFF>(waves, stages);
+        case 4: return pick_shape<D, 4, QBF16, AFF>(waves, stages);
+        case 8: return pick_shape<D, 8, QBF16, AFF>(waves, stages);
+        case 16: return pick_shape<D, 16, QBF16, AFF>(waves, stages);
         default: return nullptr;
     }
 }
 
-template <int D, bool QBF16>
+template <int D, bool QBF16, bool AFF>
 LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
 #define Q8K4V_CASE(RB_, W_, S_) \
-    if (rows_per_wg == 16 * RB_ && waves == W_ && stages == S_) return &launch_rows_t<D, RB_, W_, S_, QBF16>;
+    if (rows_per_wg == 16 * RB_ && waves == W_ && stages == S_) return &launch_rows_t<D, RB_, W_, S_, QBF16, AFF>;
+    if (AFF) {
+        Q8K4V_CASE(1, 4, 2) Q8K4V_CASE(2, 4, 2) Q8K4V_CASE(1, 8, 2) Q8K4V_CASE(2, 8, 2)
+        return nullptr;
+    }
     Q8K4V_CASE(1, 2, 2) Q8K4V_CASE(1, 2, 3) Q8K4V_CASE(1, 4, 2) Q8K4V_CASE(1, 4, 3)
     Q8K4V_CASE(2, 2, 2) Q8K4V_CASE(2, 2, 3) Q8K4V_CASE(2, 4, 2) Q8K4V_CASE(2, 4, 3)
     Q8K4V_CASE(1, 8, 2) Q8K4V_CASE(2, 8, 2) Q8K4V_CASE(1, 8, 3) Q8K4V_CASE(2, 8, 3)
@@ -899,10 +1015,14 @@ int32_t launch_cascade_fused(const AttnParams& pre, const AttnParams& suf, int h
 
 int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
     LaunchFn fn = nullptr;
-    if (head_dim == 128) fn = qbf16 ? pick_rows<128, true>(plan.rows_per_wg, plan.waves, plan.stages)
-                                    : pick_rows<128, false>(plan.rows_per_wg, plan.waves, plan.stages);
-    else fn = qbf16 ? pick_rows<64, true>(plan.rows_per_wg, plan.waves, plan.stages)
-                    : pick_rows<64, false>(plan.rows_per_wg, plan.waves, plan.stages);
+    const int rw = plan.rows_per_wg, wv = plan.waves, st = plan.stages;
+    if (kp.affine) {
+        if (head_dim == 128) fn = qbf16 ? pick_rows<128, true, true>(rw, wv, st) : pick_rows<128, false, true>(rw, wv, st);
+        else fn = qbf16 ? pick_rows<64, true, true>(rw, wv, st) : pick_rows<64, false, true>(rw, wv, st);
+    } else {
+        if (head_dim == 128) fn = qbf16 ? pick_rows<128, true, false>(rw, wv, st) : pick_rows<128, false, false>(rw, wv, st);
+        else fn = qbf16 ? pick_rows<64, true, false>(rw, wv, st) : pick_rows<64, false, false>(rw, wv, st);
+    }
     if (!fn) return fail(Q8K4V_EUNSUPPORTED, "attention: no row-block kernel for this rows/waves/stages combination");
     const hipError_t e = fn(kp, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -911,8 +1031,14 @@ int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool q
 
 int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
     LaunchFn fn = nullptr;
-    if (head_dim == 128) fn = qbf16 ? pick<128, true>(plan.rows, plan.waves, plan.stages) : pick<128, false>(plan.rows, plan.waves, plan.stages);
-    else fn = qbf16 ? pick<64, true>(plan.rows, plan.waves, plan.stages) : pick<64, false>(plan.rows, plan.waves, plan.stages);
+    const int r = plan.rows, wv = plan.waves, st = plan.stages;
+    if (kp.affine) {
+        if (head_dim == 128) fn = qbf16 ? pick<128, true, true>(r, wv, st) : pick<128, false, true>(r, wv, st);
+        else fn = qbf16 ? pick<64, true, true>(r, wv, st) : pick<64, false, true>(r, wv, st);
+    } else {
+        if (head_dim == 128) fn = qbf16 ? pick<128, true, false>(r, wv, st) : pick<128, false, false>(r, wv, st);
+        else fn = qbf16 ? pick<64, true, false>(r, wv, st) : pick<64, false, false>(r, wv, st);
+    }
     if (!fn) return fail(Q8K4V_EUNSUPPORTED, "attention: no paged-MFMA kernel for this rows/waves/stages combination");
     const hipError_t e = fn(kp, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

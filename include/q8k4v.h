@@ -66,7 +66,22 @@ extern "C" {
 #define Q8K4V_PAGE_SIZE 16
 #define Q8K4V_MAX_DRAFT 16
 
-/* The paged cache: four device pools in the layout above. */
+#define Q8K4V_CODEC_SYMMETRIC 0   /* the codec above                            */
+#define Q8K4V_CODEC_AFFINE    1   /* the affine variant below                   */
+
+/* The paged cache: four device pools in the layout above, plus two zero-point
+ * pools for the affine variant.
+ *
+ * Affine variant (the same page names the codec affine; unsigned codes with a
+ * zero point, the block's range widened to include zero):
+ *   lo = min(min x, 0), hi = max(max x, 0), s = fp16((hi - lo) / q),
+ *   z = clamp(rint(-lo / s), 0, q), code = clamp(rint(x / s) + z, 0, q),
+ *   value = (code - z) * s; q = 255 for keys (per token and kv head), 15 for
+ *   values (per token, kv head and 32 dims); s == 0 gives code and z 0.
+ *   k_codes hold code XOR 0x80 (code - 128 as int8), k_zeros z XOR 0x80;
+ *   value nibbles hold the unsigned codes, v_zeros one byte (0..15) per
+ *   (token, group).  Attention on an affine cache runs on variants 4 and 5
+ *   (and the automatic choice); variants 1-3 return EUNSUPPORTED. */
 typedef struct q8k4v_cache {
     int32_t   num_pages;     /* P: physical pages in each pool                   */
     int32_t   num_kv_heads;  /* H                                                */
@@ -76,6 +91,9 @@ typedef struct q8k4v_cache {
     uint16_t *k_scales;      /* device [P][H][16]                                */
     uint8_t  *v_codes;       /* device [P][H][D][8]                              */
     uint16_t *v_scales;      /* device [P][H][16][D/32]                          */
+    int32_t   codec;         /* Q8K4V_CODEC_SYMMETRIC (0) or Q8K4V_CODEC_AFFINE  */
+    int8_t   *k_zeros;       /* device [P][H][16], affine only (else NULL)       */
+    uint8_t  *v_zeros;       /* device [P][H][16][D/32], affine only (else NULL) */
 } q8k4v_cache;
 
 /* Launch configuration of the attention kernels (what the tuner chooses).
@@ -214,7 +232,8 @@ int32_t attn_decode_prefix_q8k4v(const q8k4v_cache *cache, const void *q, int32_
                                  hipStream_t stream);
 
 /* Workspace (bytes) of attn_decode_prefix_q8k4v: both passes' split
- * partials (no counters, nothing to zero).  Returns 0 on invalid shapes. */
+ * partials (no counters, nothing to zero), enough for either codec.
+ * Returns 0 on invalid shapes. */
 size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_seq_len, int32_t n_prefix_pages,
                                     const q8k4v_config *cfg);

@@ -14,8 +14,8 @@ def to_dev(a: np.ndarray, dtype: str = None):
     return t.cuda()
 
 
-def upload_cache(w, extra_pages: int = 0) -> q8.PagedKVCache:
-    cache = q8.PagedKVCache(w.num_pages + extra_pages, w.num_kv_heads, w.head_dim)
+def upload_cache(w, extra_pages: int = 0, codec: str = "symmetric") -> q8.PagedKVCache:
+    cache = q8.PagedKVCache(w.num_pages + extra_pages, w.num_kv_heads, w.head_dim, codec=codec)
     for a in w.appends:
         q8.kv_quant_append(cache, to_dev(a.k, w.dtype), to_dev(a.v, w.dtype), to_dev(a.cu_new),
                            to_dev(a.start_pos), to_dev(a.page_table))
@@ -24,12 +24,16 @@ def upload_cache(w, extra_pages: int = 0) -> q8.PagedKVCache:
 
 
 def cache_to_host(cache: q8.PagedKVCache) -> dict:
-    return {
+    d = {
         "k_codes": cache.k_codes.cpu().numpy(),
         "k_scales": cache.k_scales.cpu().numpy().view(np.uint16),
         "v_codes": cache.v_codes.cpu().numpy(),
         "v_scales": cache.v_scales.cpu().numpy().view(np.uint16),
     }
+    if cache.codec == "affine":
+        d["k_zeros"] = cache.k_zeros.cpu().numpy()
+        d["v_zeros"] = cache.v_zeros.cpu().numpy()
+    return d
 
 
 def run_attention(w, cache, cfg=None, q=None, seq_lens=None, max_seq_len=None):

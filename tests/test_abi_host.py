@@ -100,6 +100,23 @@ def test_workspace_size_follows_the_plan(lib):
     assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(variant=2)) == 0  # 1 row: no block MFMA
 
 
+def test_affine_cache_validation(lib):
+    """An affine cache needs its zero-point pools; its attention runs on
+    variants 4 and 5 only; an unknown codec is refused (all before a launch)."""
+    d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, q8.CODEC_AFFINE, None, None)
+    args = (1, 1, 1, 1, 32, 1, 64, 1, 4, 0.1)
+    assert lib.attn_decode_q8k4v(C.byref(d), *args, None, None, 0, None) == -1
+    assert b"k_zeros" in lib.q8k4v_last_error()
+    assert lib.kv_quant_append(C.byref(d), 1, 1, 1, 1, 1, 1, 4, 1, 1, None) == -1
+    d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, 7, 1, 1)
+    assert lib.attn_decode_q8k4v(C.byref(d), *args, None, None, 0, None) == -1
+    d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, q8.CODEC_AFFINE, 1, 1)
+    for v in (1, 2, 3):
+        cfg = q8.make_config(variant=v)
+        assert lib.attn_decode_q8k4v(C.byref(d), *args, C.byref(cfg), None, 0, None) == -2, v
+        assert b"affine" in lib.q8k4v_last_error()
+
+
 def test_prefix_cascade_validation_and_workspace(lib):
     """The shared-prefix entry point validates its page count on the host
     (before any launch) and sizes its workspace as prefix + suffix partials."""

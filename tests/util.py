@@ -11,8 +11,8 @@ from oracle import attention, codec
 ATOL_SIGMA = 2e-3
 
 
-def oracle_cache(w, extra_pages: int = 0) -> codec.PagedCache:
-    cache = codec.PagedCache(w.num_pages + extra_pages, w.num_kv_heads, w.head_dim)
+def oracle_cache(w, extra_pages: int = 0, codec_name: str = "symmetric") -> codec.PagedCache:
+    cache = codec.PagedCache(w.num_pages + extra_pages, w.num_kv_heads, w.head_dim, codec=codec_name)
     for a in w.appends:
         codec.append(cache, a.k, a.v, w.dtype, a.cu_new, a.start_pos, a.page_table)
     return cache
