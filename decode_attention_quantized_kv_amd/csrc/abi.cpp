@@ -142,7 +142,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     if (a.num_q_heads < 1 || a.num_q_heads % H) return fail(Q8K4V_EINVAL, "attention: num_q_heads must be a positive multiple of num_kv_heads");
     const int32_t G = a.num_q_heads / H;
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(Q8K4V_EUNSUPPORTED, "attention: group size num_q_heads/num_kv_heads must be 1, 2, 4 or 8");
-    if (a.n_draft < 1 || a.n_draft > Q8K4V_MAX_DRAFT) return fail(Q8K4V_EINVAL, "attention: n_draft must be in 1..16");
+    if (a.n_draft < 1 || a.n_draft > Q8K4V_MAX_CHUNK) return fail(Q8K4V_EINVAL, "attention: n_draft must be in 1..1024");
     if (a.max_seq_len < 0) return fail(Q8K4V_EINVAL, "attention: max_seq_len must be >= 0");
     if (a.max_pages < 1 || (int64_t)a.max_pages * Q8K4V_PAGE_SIZE < a.max_seq_len)
         return fail(Q8K4V_EINVAL, "attention: max_pages * 16 must cover max_seq_len");
@@ -563,6 +563,17 @@ int32_t attn_decode_prefix_q8k4v(const q8k4v_cache* cache, const void* q, int32_
         return rc;
     }
     return launch_cascade(a, n_prefix_pages, cp, workspace, workspace_bytes, stream);
+}
+
+int32_t attn_prefill_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out, int32_t n_seqs,
+                           int32_t num_q_heads, int32_t n_new, const int32_t* seq_lens, int32_t max_seq_len,
+                           const int32_t* page_table, int32_t max_pages, float softmax_scale,
+                           const q8k4v_config* cfg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n_new < 1 || n_new > Q8K4V_MAX_CHUNK) return fail(Q8K4V_EINVAL, "attn_prefill_q8k4v: n_new must be in 1..1024");
+    if (max_seq_len < n_new) return fail(Q8K4V_EINVAL, "attn_prefill_q8k4v: max_seq_len must hold the new tokens");
+    return attention_entry("attn_prefill_q8k4v", cache, q, q_dtype, out, n_seqs, num_q_heads, n_new, seq_lens,
+                           max_seq_len, page_table, max_pages, softmax_scale, cfg, workspace, workspace_bytes,
+                           stream);
 }
 
 int32_t attn_verify_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out, int32_t n_seqs,

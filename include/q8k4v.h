@@ -65,6 +65,7 @@ extern "C" {
 
 #define Q8K4V_PAGE_SIZE 16
 #define Q8K4V_MAX_DRAFT 16
+#define Q8K4V_MAX_CHUNK 1024     /* new tokens per sequence in one prefill call */
 
 #define Q8K4V_CODEC_SYMMETRIC 0   /* the codec above                            */
 #define Q8K4V_CODEC_AFFINE    1   /* the affine variant below                   */
@@ -157,7 +158,8 @@ int32_t kv_quant_append(const q8k4v_cache *cache, const void *k_new, const void 
 /*
  * Workspace (bytes) that attn_decode_q8k4v / attn_verify_q8k4v need for the
  * given launch shape and configuration (cfg may be NULL for the defaults);
- * n_draft = 0 for decode.  Returns 0 on invalid shapes.  The workspace holds
+ * n_draft = 0 for decode, the draft count for verify, the chunk length for
+ * prefill.  Returns 0 on invalid shapes.  The workspace holds
  * the split-K partials and, with fused_combine, a counter area that must be
  * zero when first used; the library leaves the counters at zero after each
  * completed call, so zero the workspace once after allocating it.
@@ -264,6 +266,29 @@ int32_t attn_verify_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
                           const int32_t *page_table, int32_t max_pages, float softmax_scale,
                           const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * attn_prefill_q8k4v -- chunked-prefill attention over the quantized cache:
+ * n_new new tokens per sequence (already appended) attend the cache, causal
+ * among themselves -- the computation of attn_verify_q8k4v for chunks of up
+ * to Q8K4V_MAX_CHUNK tokens (blog.123qwe.co.kr/?p=3927, section 3: the
+ * service cost weights 4k and 64k prompt prefill).  New token j of sequence
+ * b attends positions 0 .. seq_lens[b] - n_new + j.  The (n_new * group) x D
+ * query block of each kv head runs on the 16x16 MFMA row-block kernel in
+ * 16- or 32-row chunks; every chunk streams the context (chunks of one
+ * context range run together and share it through L2).
+ *
+ *   q, out   [n_seqs][n_new][num_q_heads][D] (q dtype q_dtype, out float32)
+ *   n_new    1 .. Q8K4V_MAX_CHUNK; every seq_lens[b] >= n_new
+ *   workspace  at least q8k4v_workspace_bytes(..., n_draft = n_new, cfg)
+ * Other arguments and errors as attn_verify_q8k4v.
+ */
+int32_t attn_prefill_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dtype,
+                           float *out, int32_t n_seqs, int32_t num_q_heads, int32_t n_new,
+                           const int32_t *seq_lens, int32_t max_seq_len,
+                           const int32_t *page_table, int32_t max_pages, float softmax_scale,
+                           const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * tune_select -- on-device search of the attention launch configuration

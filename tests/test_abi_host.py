@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select",
-              "attn_decode_prefix_q8k4v", "q8k4v_prefix_workspace_bytes"):
+              "attn_decode_prefix_q8k4v", "q8k4v_prefix_workspace_bytes", "attn_prefill_q8k4v"):
         assert n in names
 
 
@@ -81,6 +81,11 @@ def test_attention_rejects_bad_arguments(lib):
     assert dec(n=0) == -1
     assert dec(q=None) == -1
     assert lib.attn_verify_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 17, 1, 64, 1, 4, 0.1, None, None, 0, None) == -1
+    # prefill chunks: 1 .. 1024 new tokens, held by max_seq_len
+    assert lib.attn_prefill_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 1025, 1, 2048, 1, 128, 0.1, None, None, 0, None) == -1
+    assert lib.attn_prefill_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 0, 1, 64, 1, 4, 0.1, None, None, 0, None) == -1
+    assert lib.attn_prefill_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 100, 1, 64, 1, 4, 0.1, None, None, 0, None) == -1
+    assert q8.workspace_bytes(1, 32, 8, 128, 65536, 1024) > 0
     assert lib.attn_verify_q8k4v(C.byref(d), 1, 1, 1, 1, 8, 3, 1, 2, 1, 4, 0.1, None, None, 0, None) == -1
     # workspace too small (needs split partials at this length)
     d2 = q8.CacheDesc(4096, 8, 128, 16, 1, 1, 1, 1)
