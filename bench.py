@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--contiguous-pages", action="store_true", help="identity page table (profiling)")
     ap.add_argument("--codec", default="symmetric", choices=["symmetric", "affine"],
                     help="cache codec (affine: unsigned codes with zero points)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="decode steps: the append kernel, then the attention launch")
     ap.add_argument("--no-cascade", action="store_true",
                     help="shared-prefix workload: plain decode instead of the prefix cascade")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -146,8 +148,16 @@ def main() -> int:
         else:
             q8.attn_decode_q8k4v(c, q, seq_lens, msl, page_table, w.softmax_scale, out=out, cfg=cfg, workspace=ws)
 
+    # decode steps append their token inside the attention launch where the
+    # plan allows (attn_decode_append_q8k4v); other steps append, then attend
+    fused_step = not nd and not n_pref and not args.separate_append
+
     def step(i):
         c = caches[i % layers]
+        if fused_step:
+            q8.attn_decode_append_q8k4v(c, step_k, step_v, q, seq_lens, msl, page_table, w.softmax_scale, out=out,
+                                        cfg=cfg, workspace=ws)
+            return
         q8.kv_quant_append(c, step_k, step_v, step_cu, step_pos, page_table, total_new=B)
         attend(c)
 

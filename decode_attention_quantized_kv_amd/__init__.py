@@ -99,6 +99,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
                                              C.c_float, C.POINTER(Config), vp, sz, vp]
     lib.q8k4v_prefix_workspace_bytes.restype = sz
     lib.q8k4v_prefix_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(Config)]
+    lib.attn_decode_append_q8k4v.restype = i32
+    lib.attn_decode_append_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, vp, i32, vp, i32, vp, i32, i32, vp, i32, vp,
+                                             i32, C.c_float, C.POINTER(Config), vp, sz, vp]
     lib.attn_prefill_q8k4v.restype = i32
     lib.attn_prefill_q8k4v.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, i32, vp, i32, vp, i32,
                                        C.c_float, C.POINTER(Config), vp, sz, vp]
@@ -277,6 +280,30 @@ def attn_decode_prefix_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int,
     return out
 
 
+def attn_decode_append_q8k4v(cache: PagedKVCache, k_new, v_new, q, seq_lens, max_seq_len: int, page_table,
+                             softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
+                             workspace=None, stream=None):
+    """One decode step: appends ``k_new``/``v_new`` ``[B][H][D]`` (each
+    sequence's new token, at position ``seq_lens[b] - 1``) and returns the
+    decode of ``q [B][Hq][D]`` over the cache including it."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if workspace is None:
+        workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, 0, cfg), q.device)
+    rc = lib.attn_decode_append_q8k4v(C.byref(cache.desc), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q),
+                                      _dtype_code(q), _ptr(out), B, Hq, _ptr(seq_lens), int(max_seq_len),
+                                      _ptr(page_table), int(page_table.shape[1]), float(softmax_scale),
+                                      C.byref(cfg) if cfg is not None else None, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("attn_decode_append_q8k4v", rc)
+    return out
+
+
 def attn_prefill_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_table,
                        softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
                        workspace=None, stream=None):
@@ -367,6 +394,6 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
 
 
 __all__ = ["kv_quant_append", "attn_decode_q8k4v", "attn_decode_prefix_q8k4v", "attn_verify_q8k4v",
-           "attn_prefill_q8k4v", "tune_select",
+           "attn_prefill_q8k4v", "attn_decode_append_q8k4v", "tune_select",
            "workspace_bytes", "prefix_workspace_bytes",
            "PagedKVCache", "Config", "make_config", "load_library", "version", "Q8K4VError", "LIB_PATH"]

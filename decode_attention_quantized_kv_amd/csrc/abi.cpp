@@ -26,6 +26,8 @@ int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool q
 int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
 int32_t launch_combine_cascade(const AttnParams& kp, int head_dim, hipStream_t stream);
 bool cascade_fusable(const Plan& pre, const Plan& suf);
+bool decode_append_fusable(const Plan& plan, const q8k4v_cache& c);
+int32_t launch_dec2_append(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_cascade_fused(const AttnParams& pre, const AttnParams& suf, int head_dim, bool qbf16, int rows,
                              hipStream_t stream);
 
@@ -438,7 +440,7 @@ int32_t kv_quant_append(const q8k4v_cache* cache, const void* k_new, const void*
     if (total_new == 0) return Q8K4V_OK;
     if (!k_new || !v_new || !cu_new || !start_pos || !page_table)
         return fail(Q8K4V_EINVAL, "kv_quant_append: NULL input pointer");
-    AppendArgs a{cache, k_new, v_new, dtype, cu_new, start_pos, page_table, max_pages, n_seqs, total_new};
+    AppendArgs a{cache, k_new, v_new, dtype, cu_new, start_pos, page_table, max_pages, n_seqs, total_new, nullptr};
     return launch_append(a, stream);
 }
 
@@ -563,6 +565,44 @@ int32_t attn_decode_prefix_q8k4v(const q8k4v_cache* cache, const void* q, int32_
         return rc;
     }
     return launch_cascade(a, n_prefix_pages, cp, workspace, workspace_bytes, stream);
+}
+
+int32_t attn_decode_append_q8k4v(const q8k4v_cache* cache, const void* k_new, const void* v_new, int32_t new_dtype,
+                                 const void* q, int32_t q_dtype, float* out, int32_t n_seqs, int32_t num_q_heads,
+                                 const int32_t* seq_lens, int32_t max_seq_len, const int32_t* page_table,
+                                 int32_t max_pages, float softmax_scale, const q8k4v_config* cfg, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    const char* name = "attn_decode_append_q8k4v";
+    if (!k_new || !v_new) return fail(Q8K4V_EINVAL, std::string(name) + ": NULL k_new / v_new");
+    if (new_dtype != Q8K4V_F32 && new_dtype != Q8K4V_BF16) return fail(Q8K4V_EINVAL, std::string(name) + ": new_dtype must be F32 or BF16");
+    if (max_seq_len < 1) return fail(Q8K4V_EINVAL, std::string(name) + ": max_seq_len must count the new token");
+    AttnArgs a{cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens, max_seq_len, page_table, max_pages,
+               softmax_scale};
+    Plan plan;
+    int32_t rc = make_plan(a, cfg, &plan);
+    if (rc != Q8K4V_OK) {
+        g_last_error = std::string(name) + ": " + g_last_error;
+        return rc;
+    }
+    const size_t need = plan_workspace(plan);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(Q8K4V_EWORKSPACE, std::string(name) + ": workspace needs " + std::to_string(need) + " bytes");
+    if (decode_append_fusable(plan, *cache)) {
+        AttnParams kp = launch_params(a, plan, workspace);
+        kp.k_new = k_new;
+        kp.v_new = v_new;
+        kp.new_bf16 = new_dtype == Q8K4V_BF16;
+        const int D = cache->head_dim;
+        rc = launch_dec2_append(kp, plan, D, q_dtype == Q8K4V_BF16, stream);
+        if (rc != Q8K4V_OK) return rc;
+        if (!kp.direct && !kp.fused) return launch_combine(kp, D, plan.rows_per_wg, stream);
+        return Q8K4V_OK;
+    }
+    // other plans: the append kernel (one token per sequence), then the decode
+    AppendArgs ap{cache, k_new, v_new, new_dtype, nullptr, nullptr, page_table, max_pages, n_seqs, n_seqs, seq_lens};
+    rc = launch_append(ap, stream);
+    if (rc != Q8K4V_OK) return rc;
+    return launch_attention(a, plan, workspace, workspace_bytes, stream);
 }
 
 int32_t attn_prefill_q8k4v(const q8k4v_cache* cache, const void* q, int32_t q_dtype, float* out, int32_t n_seqs,

@@ -25,98 +25,12 @@
 // (slots 2j and 2j+1 of a page, dimension-major rows); when both tokens of a
 // pair are new in the same call, the even token's wavefront quantizes the odd
 // token's values too and writes the whole byte, so no byte has two writers.
+#include "codec_device.h"
 #include "q8k4v_device.h"
 #include "q8k4v_internal.h"
 
 namespace q8k4v {
 namespace {
-
-template <int D, bool BF16>
-Q8K4V_DEV void load_row(const void* base, size_t row, int lane, float (&x)[D / 64]) {
-    constexpr int EPL = D / 64;
-    if (BF16) {
-        const uint16_t* p = (const uint16_t*)base + row * D + EPL * lane;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = bf16_to_f32(p[e]);
-    } else {
-        const float* p = (const float*)base + row * D + EPL * lane;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = p[e];
-    }
-}
-
-Q8K4V_DEV float wave_max(float x, int lanes) {
-    for (int m = 1; m < lanes; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
-Q8K4V_DEV float wave_min(float x, int lanes) {
-    for (int m = 1; m < lanes; m <<= 1) x = fminf(x, __shfl_xor(x, m));
-    return x;
-}
-
-// fp16 scale of an absmax: IEEE fp32 division, RNE into fp16, saturating.
-Q8K4V_DEV _Float16 scale_of(float absmax, float qmax) {
-    const float s32 = absmax / qmax;
-    _Float16 s16 = (_Float16)s32;
-    if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
-    return s16;
-}
-
-Q8K4V_DEV int code_of(float x, float s, float qmax) {
-    if (s == 0.0f) return 0;
-    float r = rintf(x / s);
-    r = fminf(fmaxf(r, -qmax), qmax);
-    return (int)r;
-}
-
-// Affine block parameters from the block's min and max (over the lanes that
-// hold it): fp16 scale and zero point.
-struct Affine {
-    _Float16 s16;
-    float s, z;
-};
-
-Q8K4V_DEV Affine affine_of(float mn, float mx, float qmax) {
-    const float lo = fminf(mn, 0.0f), hi = fmaxf(mx, 0.0f);
-    Affine a;
-    a.s16 = scale_of(hi - lo, qmax);
-    a.s = (float)a.s16;
-    a.z = (a.s == 0.0f) ? 0.0f : fminf(fmaxf(rintf(-lo / a.s), 0.0f), qmax);
-    return a;
-}
-
-Q8K4V_DEV int affine_code(float x, const Affine& a, float qmax) {
-    if (a.s == 0.0f) return 0;
-    return (int)fminf(fmaxf(rintf(x / a.s) + a.z, 0.0f), qmax);
-}
-
-// Value codes of one token for this lane's dimensions (nibble values: two's
-// complement when symmetric, unsigned when affine), with its group's scale
-// (and zero point) reduced over the LPG lanes of the group.
-template <int EPL, int LPG, bool AFF>
-Q8K4V_DEV void value_codes(const float (&x)[EPL], int (&c)[EPL], _Float16* s16, int* z) {
-    if (AFF) {
-        float mn = x[0], mx = x[0];
-#pragma unroll
-        for (int e = 1; e < EPL; ++e) { mn = fminf(mn, x[e]); mx = fmaxf(mx, x[e]); }
-        const Affine a = affine_of(wave_min(mn, LPG), wave_max(mx, LPG), 15.0f);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) c[e] = affine_code(x[e], a, 15.0f);
-        *s16 = a.s16;
-        *z = (int)a.z;
-    } else {
-        float va = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) va = fmaxf(va, fabsf(x[e]));
-        va = wave_max(va, LPG);
-        *s16 = scale_of(va, 7.0f);
-        const float vs = (float)*s16;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) c[e] = code_of(x[e], vs, 7.0f);
-        *z = 0;
-    }
-}
 
 template <int D, bool BF16, bool AFF>
 __global__ __launch_bounds__(256) void append_kernel(
@@ -126,7 +40,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const int32_t* __restrict__ cu_new, const int32_t* __restrict__ start_pos,
     const int32_t* __restrict__ page_table, int32_t max_pages, int32_t n_seqs,
-    int32_t total_new) {
+    int32_t total_new, const int32_t* __restrict__ last_of) {
     constexpr int EPL = D / 64;      // elements per lane
     constexpr int NG = D / 32;       // value groups
     constexpr int LPG = 32 / EPL;    // lanes per value group
@@ -136,16 +50,23 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int tok = (int)(item / H);
     const int h = (int)(item % H);
 
-    // sequence of this token: the largest b with cu_new[b] <= tok
-    int lo = 0, hi = n_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+    int b, first, last, pos;
+    if (last_of) {                    // one token per sequence, at position last_of[b] - 1
+        b = first = tok;
+        last = tok + 1;
+        pos = last_of[b] - 1;
+    } else {
+        // sequence of this token: the largest b with cu_new[b] <= tok
+        int lo = 0, hi = n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu_new[mid] <= tok) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        first = cu_new[b];
+        last = cu_new[b + 1];
+        pos = start_pos[b] + (tok - first);
     }
-    const int b = lo;
-    const int first = cu_new[b];
-    const int last = cu_new[b + 1];
-    const int pos = start_pos[b] + (tok - first);
     const int page = page_table[(size_t)b * max_pages + (pos >> 4)];
     const int slot = pos & 15;
     const size_t blk = (size_t)page * H + h;
@@ -229,7 +150,7 @@ int32_t launch_append(const AppendArgs& a, hipStream_t stream) {
 #define Q8K4V_APPEND(DD, BB, AA)                                                                      \
     hipLaunchKernelGGL((append_kernel<DD, BB, AA>), grid, block, 0, stream, c.k_codes, c.k_scales,    \
                        c.v_codes, c.v_scales, c.k_zeros, c.v_zeros, c.num_kv_heads, a.k_new, a.v_new, \
-                       a.cu_new, a.start_pos, a.page_table, a.max_pages, a.n_seqs, a.total_new)
+                       a.cu_new, a.start_pos, a.page_table, a.max_pages, a.n_seqs, a.total_new, a.last_of)
     const bool bf = a.dtype == Q8K4V_BF16;
     const bool aff = c.codec == Q8K4V_CODEC_AFFINE;
     if (c.head_dim == 128) {

@@ -40,6 +40,11 @@ struct AttnParams {
     int32_t affine;
     const int8_t* __restrict__ k_zeros;
     const uint8_t* __restrict__ v_zeros;
+    // decode that appends the step's token itself: K and V rows [n_seqs][H][D]
+    // of the token at position seq_lens[b] - 1 (bf16 bit patterns or fp32)
+    const void* __restrict__ k_new;
+    const void* __restrict__ v_new;
+    int32_t new_bf16;
 };
 
 constexpr float kNegInf = -__builtin_inff();

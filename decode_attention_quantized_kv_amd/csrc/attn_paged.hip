@@ -32,6 +32,7 @@
 //    Output tile dt (dims 16dt .. 16dt+15, value group dt/2) keeps the rows
 //    of its group.
 #include "attn_common.h"
+#include "codec_device.h"
 #include "q8k4v_internal.h"
 
 namespace q8k4v {
@@ -130,7 +131,7 @@ Q8K4V_DEV void value_zero_pairs(const uint32_t* vz0, const uint32_t* vz1, int g,
 // The kernel bodies take their tile ring (WAVES x STAGES stages, in LDS) and
 // their block index as arguments so that one launch can run two of them
 // (the shared-prefix cascade's fused pass).
-template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
+template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF, bool APP = false>
 Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;                      // pages per tile
     constexpr int KB = 16 * D, VB = 8 * D;     // key / value code bytes per page
@@ -167,6 +168,35 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     const int kh = w.kh, pend = w.pend;
     const int ntile_all = (pend - w.pbeg + TP - 1) / TP;
     const int nt = ntile_all > wave ? (ntile_all - wave + WAVES - 1) / WAVES : 0;   // <= 32 (planner)
+
+    // APP: the step's new token sits at position L - 1, logical page pn; the
+    // wave whose tile holds pn quantizes it (the append kernel's rule, same
+    // device functions), patches its slot in that tile's LDS copy before the
+    // tile is read and writes it to the cache for later calls -- this launch
+    // never reads the token from memory
+    constexpr int EPL = D / 64;
+    bool app_owner = false;
+    int app_t = -1, app_u = 0, app_slot = 0;
+    if (APP) {
+        const int pn = (w.L - 1) >> 4;
+        if (w.L > 0 && pn >= w.pbeg && pn < pend && ((pn - w.pbeg) / TP) % WAVES == wave) {
+            app_owner = true;
+            app_t = ((pn - w.pbeg) / TP) / WAVES;
+            app_u = (pn - w.pbeg) % TP;
+            app_slot = (w.L - 1) & 15;
+        }
+    }
+    float app_kx[EPL], app_vx[EPL];
+    if (APP && app_owner) {   // loads go out before the query's, so one wait covers both
+        const size_t row = (size_t)w.b * p.H + kh;
+        if (p.new_bf16) {
+            load_row<D, true>(p.k_new, row, lane, app_kx);
+            load_row<D, true>(p.v_new, row, lane, app_vx);
+        } else {
+            load_row<D, false>(p.k_new, row, lane, app_kx);
+            load_row<D, false>(p.v_new, row, lane, app_vx);
+        }
+    }
 
     // page ids of this wave's tiles, one per lane: page u of wave tile t is
     // lane 2t + u (pages past the split end repeat its last page; masked)
@@ -281,6 +311,19 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
         lim = w.L - p.W + 1 + row / p.G;
         if (AFF) qsum = xgroups_isum(qsum);
     }
+    // APP: codes and scales of the new token (symmetric codec)
+    int app_kc[EPL] = {}, app_vc[EPL] = {};
+    _Float16 app_ks16 = 0, app_vs16 = 0;
+    if (APP && app_owner) {
+        float ka = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ka = fmaxf(ka, fabsf(app_kx[e]));
+        app_ks16 = scale_of(wave_max(ka, 64), 127.0f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) app_kc[e] = code_of(app_kx[e], (float)app_ks16, 127.0f);
+        int z;
+        value_codes<EPL, 32 / EPL, false>(app_vx, app_vc, &app_vs16, &z);
+    }
     const int lim_min = w.L - p.W + 1;         // every row sees the positions below this
 
     float m_run = kNegInf, l_run = 0.0f;       // row `row`; l_run over this lane's tokens
@@ -300,6 +343,35 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
         else if (after >= 1) wait_vmem<IPT>();
         else wait_vmem<0>();
 
+        if (APP && app_owner && t == app_t) {
+            // the new token's slot in this tile's LDS copy, then the cache
+            uint8_t* sw = stage0 + slot * STAGE;
+            const int id = __builtin_amdgcn_readlane(my_id, TP * app_t + app_u);
+            const size_t blk = (size_t)id * p.H + kh;
+            int8_t* kdst = const_cast<int8_t*>(p.k_codes) + (blk * 16 + app_slot) * D;
+            uint8_t* vdst = const_cast<uint8_t*>(p.v_codes) + blk * 8 * D;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int d = EPL * lane + e, c = d / 16;
+                sw[app_u * KB + (app_slot * CPR + (c ^ (app_slot % CPR))) * 16 + d % 16] = (uint8_t)app_kc[e];
+                kdst[d] = (int8_t)app_kc[e];
+                uint8_t* vb = sw + OFF_V + app_u * VB + d * 8 + (app_slot >> 1);
+                const uint32_t nib = (uint32_t)app_vc[e] & 0xFu;
+                const uint8_t byte = (uint8_t)((app_slot & 1) ? ((*vb & 0x0Fu) | (nib << 4)) : ((*vb & 0xF0u) | nib));
+                *vb = byte;
+                vdst[d * 8 + (app_slot >> 1)] = byte;
+            }
+            const uint16_t ksb = __builtin_bit_cast(uint16_t, app_ks16), vsb = __builtin_bit_cast(uint16_t, app_vs16);
+            if (lane == 0) {
+                *(uint16_t*)(sw + OFF_KS + app_u * KSB + app_slot * 2) = ksb;
+                const_cast<uint16_t*>(p.k_scales)[blk * 16 + app_slot] = ksb;
+            }
+            if (lane % (32 / EPL) == 0) {
+                const int g = lane / (32 / EPL);
+                *(uint16_t*)(sw + OFF_VS + app_u * VSB + (app_slot * NG + g) * 2) = vsb;
+                const_cast<uint16_t*>(p.v_scales)[(blk * 16 + app_slot) * NG + g] = vsb;
+            }
+        }
         // ---- tile to registers
         const uint8_t* st = stage0 + slot * STAGE;
         u32x4 ka[TP][KS];
@@ -472,6 +544,14 @@ template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
     dec2_body<D, R, WAVES, STAGES, QBF16, AFF>(p, s_stage, (int)blockIdx.x);
+}
+
+// Decode that appends the step's new token itself (four waves, two stages,
+// symmetric codec).
+template <int D, int R, bool QBF16>
+__global__ __launch_bounds__(256) void attn_dec2_append_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, false>()];
+    dec2_body<D, R, 4, 2, QBF16, false, true>(p, s_stage, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -995,7 +1075,43 @@ hipError_t pick_cascade(int rows, const AttnParams& pre, const AttnParams& suf, 
     }
 }
 
+template <int D, int R, bool QBF16>
+hipError_t launch_append_t(const AttnParams& kp, hipStream_t stream) {
+    const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
+    const int blocks = 8 * ((total + 7) / 8);
+    hipLaunchKernelGGL((attn_dec2_append_kernel<D, R, QBF16>), dim3(blocks), dim3(256), 0, stream, kp);
+    return hipGetLastError();
+}
+
+template <int D, bool QBF16>
+LaunchFn pick_append(int rows) {
+    switch (rows) {
+        case 1: return &launch_append_t<D, 1, QBF16>;
+        case 2: return &launch_append_t<D, 2, QBF16>;
+        case 4: return &launch_append_t<D, 4, QBF16>;
+        case 8: return &launch_append_t<D, 8, QBF16>;
+        case 16: return &launch_append_t<D, 16, QBF16>;
+        default: return nullptr;
+    }
+}
+
 }  // namespace
+
+// Decode with the step's token appended in the same launch: replicated-row
+// plan with four waves and two stages on a symmetric cache.
+bool decode_append_fusable(const Plan& plan, const q8k4v_cache& c) {
+    return plan.kernel == kDec2 && plan.waves == 4 && plan.stages == 2 && c.codec == Q8K4V_CODEC_SYMMETRIC;
+}
+
+int32_t launch_dec2_append(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
+    LaunchFn fn;
+    if (head_dim == 128) fn = qbf16 ? pick_append<128, true>(plan.rows) : pick_append<128, false>(plan.rows);
+    else fn = qbf16 ? pick_append<64, true>(plan.rows) : pick_append<64, false>(plan.rows);
+    if (!fn) return fail(Q8K4V_EUNSUPPORTED, "attention: no appending decode kernel for this row count");
+    const hipError_t e = fn(kp, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return Q8K4V_OK;
+}
 
 // One launch of both cascade passes (prefix plan: 32-row blocks, 4 waves, 2
 // stages; suffix plan: replicated rows, 4 or 8 rows, 4 waves, 2 stages).

@@ -25,6 +25,9 @@ struct AppendArgs {
     const int32_t* start_pos;
     const int32_t* page_table;
     int32_t max_pages, n_seqs, total_new;
+    // if set (cu_new and start_pos unused): one token per sequence, token b
+    // at position last_of[b] - 1
+    const int32_t* last_of;
 };
 int32_t launch_append(const AppendArgs& a, hipStream_t stream);
 

@@ -268,6 +268,32 @@ int32_t attn_verify_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
                           hipStream_t stream);
 
 /*
+ * attn_decode_append_q8k4v -- one decode step: kv_quant_append of each
+ * sequence's new token followed by attn_decode_q8k4v, in one attention
+ * launch where the plan allows.  The new token of sequence b goes to
+ * position seq_lens[b] - 1 (seq_lens counts it).  The cache afterwards and
+ * the output are those of the two calls (same codec rule, same device
+ * functions): the wave whose tile holds the token's page quantizes it,
+ * puts it into its LDS copy of the page before the tile is read, and writes
+ * it to the cache for later calls (blog.123qwe.co.kr/?p=3927, section 5:
+ * the decode unit over the k8v4 cache).  Fused when the decode plan is the
+ * replicated-row kernel with 4 waves and 2 stages on a symmetric cache (the
+ * defaults for 1, 2, 4, 8 or 16 rows per kv head); otherwise the append
+ * kernel runs first, then the decode.
+ *
+ *   k_new, v_new  device [n_seqs][H][D], dtype new_dtype (Q8K4V_F32 or Q8K4V_BF16)
+ *   seq_lens      device int32 [n_seqs], >= 1, the new token included
+ * Other arguments and errors as attn_decode_q8k4v (workspace from
+ * q8k4v_workspace_bytes with n_draft 0).
+ */
+int32_t attn_decode_append_q8k4v(const q8k4v_cache *cache, const void *k_new, const void *v_new,
+                                 int32_t new_dtype, const void *q, int32_t q_dtype, float *out,
+                                 int32_t n_seqs, int32_t num_q_heads, const int32_t *seq_lens,
+                                 int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
+                                 float softmax_scale, const q8k4v_config *cfg, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_prefill_q8k4v -- chunked-prefill attention over the quantized cache:
  * n_new new tokens per sequence (already appended) attend the cache, causal
  * among themselves -- the computation of attn_verify_q8k4v for chunks of up
