@@ -1,7 +1,9 @@
-// Pieces shared by the three attention kernels (vector, 4x4x4 block MFMA,
-// 16x16 MFMA): launch parameters, the XCD-aware work-item mapping, the merge
-// of a workgroup's waves, the split partials and the log-sum-exp combine of
-// the splits (by the last-arriving workgroup or by a separate kernel).
+// Pieces shared by the attention kernels (vector, 4x4x4 block MFMA, 16x16
+// MFMA, and the two tile-ring kernels of attn_paged.hip): launch parameters,
+// the XCD-aware work-item mapping, the merge of a workgroup's waves, the
+// split partials and the log-sum-exp combine of the splits (by the
+// last-arriving workgroup or by a separate kernel, and the two-source combine
+// of the shared-prefix cascade).
 #pragma once
 
 #include "q8k4v_device.h"

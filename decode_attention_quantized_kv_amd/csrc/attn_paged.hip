@@ -31,6 +31,11 @@
 //    (one 32-bit word per lane and output tile: 4 nibbles of P0, 4 of P1).
 //    Output tile dt (dims 16dt .. 16dt+15, value group dt/2) keeps the rows
 //    of its group.
+//
+// The same file holds the row-block variant for other row counts (verify,
+// chunked prefill, the cascade's prefix pass), the decode body that appends
+// the step's new token itself, the fused launch of the cascade's prefix and
+// suffix passes, and the affine-codec paths of both bodies.
 #include "attn_common.h"
 #include "codec_device.h"
 #include "q8k4v_internal.h"
@@ -901,7 +906,8 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
         }
     }
 
-    // ---- merge the waves in wave order through one [RW][D] buffer
+    // ---- merge the waves: each row's maximum, sum and wave factors, then
+    // the outputs through LDS buffers (a fixed two-round tree)
     __shared__ float s_M[RW], s_L[RW], s_f[WAVES][RW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
