@@ -591,9 +591,6 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int RW = 16 * RB;                // rows per workgroup
     constexpr int NVW = NG / 2;                // 32-bit words of one token's value scales
     static_assert(STAGES >= 2 && STAGES <= 3, "2 or 3 stages");
-    constexpr int SOS = D + 4;                 // merge-buffer row stride: lane groups 4 rows apart
-                                               // land 16 banks apart
-    static_assert(RW * SOS * 4 <= WAVES * STAGES * STAGE, "the merge buffer reuses the tile ring");
     static_assert(STAGE == ring_stage_bytes<D, AFF>(), "tile layout");
 
     __shared__ float s_ml[WAVES][RW][2];
@@ -908,7 +905,8 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 
     // ---- merge the waves: each row's maximum, sum and wave factors, then
     // the outputs through LDS buffers (a fixed two-round tree)
-    __shared__ float s_M[RW], s_L[RW], s_f[WAVES][RW];
+    __shared__ float s_M[RW], s_L[RW];
+    __shared__ __attribute__((aligned(16))) float s_f[WAVES][RW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = xgroups_sum(l_run[rb]);
@@ -935,10 +933,14 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     }
     __syncthreads();
     // two rounds into NB = WAVES/2 buffers (upper half of the waves writes,
-    // lower half adds), then one pass sums the buffers: fixed order, three
-    // barriers whatever the wave count
+    // lower half adds), then one pass sums the buffers and emits: fixed
+    // order, two barriers whatever the wave count.  The buffers are
+    // transposed, [dimension][row] with rows padded to TS: a lane's four
+    // rows 16 rb + 4 q4 .. +3 of dimension 16 dt + n16 are one 16-byte access.
     constexpr int NB = WAVES / 2;
-    constexpr int BUF = RW * SOS;
+    constexpr int TS = RW + 4;                 // 4 mod 8 words: 16-byte accesses of 8 consecutive
+                                               // dimensions hit distinct banks
+    constexpr int BUF = D * TS;
     static_assert(NB * BUF * 4 <= WAVES * STAGES * STAGE, "merge buffers reuse the tile ring");
     float* s_o = (float*)smem;
 #pragma unroll
@@ -947,33 +949,48 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
         if (mine) {
             float* buf = s_o + (wave % NB) * BUF;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+            for (int rb = 0; rb < RB; ++rb) {
+                const f32x4 f = *(const f32x4*)&s_f[wave][16 * rb + 4 * q4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rl = 16 * rb + 4 * q4 + i;
-                    const float f = s_f[wave][rl];
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        float* dst = buf + rl * SOS + 16 * dt + n16;
-                        const float v = acc[rb][dt][i] * f;
-                        *dst = (round == 0) ? v : *dst + v;
-                    }
+                for (int dt = 0; dt < NDT; ++dt) {
+                    f32x4* dst = (f32x4*)(buf + (16 * dt + n16) * TS + 16 * rb + 4 * q4);
+                    const f32x4 v = acc[rb][dt] * f;
+                    *dst = (round == 0) ? v : *dst + v;
                 }
+            }
         }
         __syncthreads();
     }
-    if (NB > 1) {
-        for (int e = threadIdx.x; e < RW * (D / 4); e += 64 * WAVES) {
-            const int rl = e / (D / 4), c4 = e % (D / 4);
-            f32x4* d0 = (f32x4*)(s_o + rl * SOS) + c4;
-            f32x4 sum = *d0;
+    // element e = (row quad r4, dimension d): lanes take consecutive
+    // dimensions, so each row's stores are contiguous
+    const size_t rs = (size_t)p.R * partial_stride<D>();
+    float* split_base = p.partials + ((size_t)w.b * p.H + w.kh) * p.n_splits * rs + w.split * rs;
+    for (int e = threadIdx.x; e < D * (RW / 4); e += 64 * WAVES) {
+        const int d = e % D, r4 = e / D;
+        f32x4 O = *(const f32x4*)(s_o + d * TS + 4 * r4);
 #pragma unroll
-            for (int b = 1; b < NB; ++b) sum += *((const f32x4*)(s_o + b * BUF + rl * SOS) + c4);
-            *d0 = sum;
+        for (int bb = 1; bb < NB; ++bb) O += *(const f32x4*)(s_o + bb * BUF + d * TS + 4 * r4);
+        const float ov[4] = {O.x, O.y, O.z, O.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int rl = 4 * r4 + k, r = r0 + rl;
+            if (r >= p.R) continue;
+            const float Ls = s_L[rl];
+            if (p.direct) {
+                const float inv = (Ls > 0.0f) ? 1.0f / Ls : 0.0f;
+                p.out[out_index(p, w.b, w.kh, r, D) + d] = ov[k] * inv;
+                continue;
+            }
+            float* rec = split_base + (size_t)r * partial_stride<D>();
+            if (p.fused) {
+                if (d == 0) { store_coherent(rec, s_M[rl]); store_coherent(rec + 1, Ls); }
+                store_coherent(rec + 4 + d, ov[k]);
+            } else {
+                if (d == 0) *(float2*)rec = float2{s_M[rl], Ls};
+                rec[4 + d] = ov[k];
+            }
         }
-        __syncthreads();
     }
-    emit_rows<D, RW, SOS>(p, w, r0, s_M, s_L, s_o);
     fused_tail<D, RW>(p, w, r0, smem, WAVES * STAGES * STAGE);
 }
 
