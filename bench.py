@@ -10,9 +10,11 @@ Prints one JSON line.  ``value`` is the achieved algorithmic HBM bandwidth of
 the whole step (GB/s); ``tok_s_per_layer`` is query tokens per second per
 layer; ``roofline`` reports the attention kernel alone, timed with HIP events
 on the stream it runs on.  ``cpu_baseline`` times the CPU oracle on the same
-workload (a bounded number of steps).
+workload (a bounded number of steps).  ``--cpu-report`` only times the CPU
+oracle on every workload, at the default BLAS pool and at one thread.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --cpu-report
 """
 
 from __future__ import annotations
@@ -60,6 +62,8 @@ def parse():
                     help="shared-prefix workload: plain decode instead of the prefix cascade")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--cpu-report", action="store_true",
+                    help="only time the CPU oracle on every workload (no GPU) and exit")
     return ap.parse_args()
 
 
@@ -69,6 +73,8 @@ def main() -> int:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the sharding design is described in DESIGN.md)"}))
         return 2
+    if args.cpu_report:
+        return cpu_report()
     import torch
 
     import decode_attention_quantized_kv_amd as q8
@@ -337,6 +343,70 @@ def cpu_baseline(w, steps: int, step_bytes: int, tokens: int) -> dict:
             "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{steps} full steps of {w.name} (median); numpy elementwise work is single-threaded, "
                       f"matmuls use the BLAS pool"}
+
+
+def cpu_report(reps: int = 3) -> int:
+    """The CPU oracle as it stands, timed on this host for every workload:
+    the quantizer filling each workload's cache, and one fp64 attention call
+    (decode, verify or the multi-session decode) over the filled cache, each
+    with the BLAS pool at its default size and limited to one thread (numpy's
+    elementwise work is single-threaded either way).  Medians of `reps` runs
+    (one run where the first takes over 60 s).  Prints one JSON line per
+    measurement."""
+    import contextlib
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import workloads
+    from oracle import attention, codec
+
+    pool = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    print(json.dumps({"host": {"sched_getaffinity": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+                               "blas_threads_default": pool, "reps": reps}}), flush=True)
+
+    def median_time(fn):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+            if ts[0] > 60.0:
+                break
+        return float(np.median(ts)), len(ts)
+
+    for name in ["tiny_decode_256", "gqa_decode_4096", "gqa_decode_65536", "verify_65536_w8",
+                 "multi_session_16x32768"]:
+        w = workloads.NAMED[name]()
+        H, D = w.num_kv_heads, w.head_dim
+        nbytes = w.unique_tokens() * H * cache_bytes_per_token_head(D)
+        tokens = w.n_seqs * max(1, w.n_draft)
+
+        def fill():
+            cache = codec.PagedCache(w.num_pages, H, D)
+            for a in w.appends:
+                codec.append(cache, a.k, a.v, w.dtype, a.cu_new, a.start_pos, a.page_table)
+            return cache
+
+        cache = fill()
+        fn = attention.verify if w.n_draft else attention.decode
+
+        def attend():
+            fn(cache, w.q, w.dtype, w.page_table, w.seq_lens, w.softmax_scale)
+
+        for threads in (None, 1):
+            limit = threadpool_limits(threads) if threads else contextlib.nullcontext()
+            with limit:
+                for what, run in (("attention", attend), ("quantize_fill", fill)):
+                    t, n = median_time(run)
+                    rec = {"workload": name, "step": what, "blas_threads": threads or pool, "runs": n,
+                           "s": round(t, 4)}
+                    if what == "attention":
+                        rec.update({"GB_s_algorithmic": round(nbytes / t / 1e9, 4),
+                                    "tok_s_per_layer": round(tokens / t, 4)})
+                    else:
+                        rec["tokens_quantized"] = int(sum(len(a.k) for a in w.appends)) * H
+                    print(json.dumps(rec), flush=True)
+    return 0
 
 
 if __name__ == "__main__":
