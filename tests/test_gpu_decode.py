@@ -56,6 +56,21 @@ def test_ragged_batch_all_groups(hq, hkv, D, dtype):
     assert np.all(got[4] == 0)
 
 
+def test_many_sequences():
+    """48 ragged sequences (lengths 0..1200, seeded): the splits of every
+    sequence are dealt over the XCDs starting at a different one per
+    sequence, and empty sequences give zero rows."""
+    from tests.gpu_util import run_attention, upload_cache
+    lens = np.random.default_rng(2024).integers(0, 1201, size=48)
+    lens[[5, 17]] = 0
+    w = workloads.build("many", seed=31, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                        seq_lens=lens.tolist(), outliers=True)
+    cache = upload_cache(w)
+    got = run_attention(w, cache)
+    _check(w, got, oracle_out(w), "48 sequences")
+    assert np.all(got[5] == 0) and np.all(got[17] == 0)
+
+
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: "default" if c is None else "-".join(f"{k}{v}" for k, v in c.items()))
 def test_every_launch_configuration(cfg):
     from tests.gpu_util import run_attention, upload_cache

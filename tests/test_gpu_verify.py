@@ -21,7 +21,7 @@ def _check(w, got, want, label):
 
 @pytest.mark.parametrize("W,hq,hkv,D", [(2, 8, 4, 128), (2, 16, 8, 128), (4, 8, 8, 128), (1, 32, 8, 128),
                                          (8, 32, 8, 128), (4, 32, 8, 128), (3, 32, 8, 128), (16, 32, 8, 128),
-                                         (8, 32, 8, 64), (5, 8, 8, 64), (8, 32, 4, 128)])
+                                         (8, 32, 8, 64), (5, 8, 8, 64), (8, 32, 4, 128), (16, 64, 8, 128)])
 def test_draft_widths_and_groups(W, hq, hkv, D):
     from tests.gpu_util import run_attention, upload_cache
     w = workloads.build("ver", seed=W * 100 + hq + D, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, dtype="bf16",
