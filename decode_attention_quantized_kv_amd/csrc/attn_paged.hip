@@ -573,7 +573,7 @@ __global__ __launch_bounds__(256) void attn_dec2_append_kernel(const AttnParams 
 //    fp16 value codes: lane (n, q) holds rows 16 rb + 4q + i, dim 16 dt + n.
 // The waves' outputs are merged in a fixed two-round tree through LDS.
 // ---------------------------------------------------------------------------
-template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
+template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF, bool SQ = false>
 Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;
     constexpr int KB = 16 * D, VB = 8 * D;
@@ -647,15 +647,31 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
     };
 
     // ---- query rows r0 + 16 rb + n as B operands (15-bit fixed point, int8
-    // halves; rows past R are zero)
+    // halves; rows past R are zero).  SQ: wave rb converts row block rb only
+    // and hands it to the others through LDS; the other waves start their
+    // first copies at once.
     u32x4 qhi[RB][KS], qlo[RB][KS];
     float coef[RB];
     int lim[RB];
     int qsum[RB];                              // sum of each row's fixed-point Q (affine keys)
-    {
+    static_assert(!SQ || WAVES >= RB, "one converting wave per row block");
+    __shared__ u32x4 s_q[SQ ? RB * KS * 2 * 64 : 1];
+    __shared__ float s_coef[SQ ? RB * 16 : 1];
+    __shared__ int s_qsum[SQ ? RB * 16 : 1];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = r0 + 16 * rb + n16;
+        lim[rb] = r < p.R ? w.L - p.W + 1 + r / p.G : 0;
+    }
+    if (SQ && wave >= RB) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nt) issue(s, s);
+    } else {
         float x[RB][KS][16];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+            if (SQ && rb != wave) continue;
             const int r = r0 + 16 * rb + n16;
             const bool ok = r < p.R;
             const size_t qoff = out_index(p, w.b, kh, ok ? r : 0, D);
@@ -683,11 +699,11 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                     }
                 }
             }
-            lim[rb] = ok ? w.L - p.W + 1 + r / p.G : 0;
         }
         float mx[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+            if (SQ && rb != wave) continue;
             mx[rb] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -700,6 +716,7 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
             if (s < nt) issue(s, s);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+            if (SQ && rb != wave) continue;
             int e = 0;
             if (mx[rb] > 0.0f) (void)frexpf(mx[rb], &e);
             e = min(max(e, -110), 110);
@@ -727,6 +744,30 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
             }
             coef[rb] = p.scale_log2 * ldexpf(1.0f, e - 14);
             qsum[rb] = AFF ? xgroups_isum(qs) : 0;
+            if (SQ) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s_q[((rb * KS + ks) * 2) * 64 + lane] = qhi[rb][ks];
+                    s_q[((rb * KS + ks) * 2 + 1) * 64 + lane] = qlo[rb][ks];
+                }
+                if (q4 == 0) {
+                    s_coef[rb * 16 + n16] = coef[rb];
+                    s_qsum[rb * 16 + n16] = qsum[rb];
+                }
+            }
+        }
+    }
+    if (SQ) {
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                qhi[rb][ks] = s_q[((rb * KS + ks) * 2) * 64 + lane];
+                qlo[rb][ks] = s_q[((rb * KS + ks) * 2 + 1) * 64 + lane];
+            }
+            coef[rb] = s_coef[rb * 16 + n16];
+            qsum[rb] = s_qsum[rb * 16 + n16];
         }
     }
     const int lim_min = w.L - p.W + 1;
@@ -997,7 +1038,10 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
-    rows_body<D, RB, WAVES, STAGES, QBF16, AFF>(p, s_stage, (int)blockIdx.x);
+    // the shared query operands (RB x 2 KiB per 64 dimensions) where the LDS
+    // budget allows them
+    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + RB * (D / 64) * 2048 + 8192 <= 163840;
+    rows_body<D, RB, WAVES, STAGES, QBF16, AFF, SQ>(p, s_stage, (int)blockIdx.x);
 }
 
 // Fused pass of the shared-prefix cascade: blocks [0, pre_blocks) run the
