@@ -136,7 +136,7 @@ Q8K4V_DEV void value_zero_pairs(const uint32_t* vz0, const uint32_t* vz1, int g,
 // The kernel bodies take their tile ring (WAVES x STAGES stages, in LDS) and
 // their block index as arguments so that one launch can run two of them
 // (the shared-prefix cascade's fused pass).
-template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF, bool APP = false>
+template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF, bool APP = false, bool SQ = false>
 Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     constexpr int TP = 2;                      // pages per tile
     constexpr int KB = 16 * D, VB = 8 * D;     // key / value code bytes per page
@@ -247,11 +247,20 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
     // 64 ks + 16 q .. +15 of every k-step ks
     // (the query loads go out with the page-id load, before the first
     // copies: the compiler's wait for them then covers no copy)
+    // (SQ: wave 0 converts and hands the operands to the other waves through
+    // LDS; those start their first copies at once)
     u32x4 qhi[KS], qlo[KS];
     float coef;
-    int lim;
     int qsum = 0;                              // sum of the row's fixed-point Q (affine keys)
-    {
+    const int lim = w.L - p.W + 1 + row / p.G;
+    __shared__ u32x4 s_q[SQ ? KS * 2 * 64 : 1];
+    __shared__ float s_coef[SQ ? 64 : 1];
+    __shared__ int s_qsum[SQ ? 64 : 1];
+    if (SQ && wave != 0) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nt) issue(s, s);
+    } else {
         const size_t qoff = out_index(p, w.b, kh, row, D);
         float x[KS][16];
 #pragma unroll
@@ -313,8 +322,26 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
             qlo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
         }
         coef = p.scale_log2 * ldexpf(1.0f, e - 14);
-        lim = w.L - p.W + 1 + row / p.G;
         if (AFF) qsum = xgroups_isum(qsum);
+        if (SQ) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s_q[(2 * ks) * 64 + lane] = qhi[ks];
+                s_q[(2 * ks + 1) * 64 + lane] = qlo[ks];
+            }
+            s_coef[lane] = coef;
+            s_qsum[lane] = qsum;
+        }
+    }
+    if (SQ) {
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qhi[ks] = s_q[(2 * ks) * 64 + lane];
+            qlo[ks] = s_q[(2 * ks + 1) * 64 + lane];
+        }
+        coef = s_coef[lane];
+        qsum = s_qsum[lane];
     }
     // APP: codes and scales of the new token (symmetric codec)
     int app_kc[EPL] = {}, app_vc[EPL] = {};
@@ -548,7 +575,8 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
 template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
-    dec2_body<D, R, WAVES, STAGES, QBF16, AFF>(p, s_stage, (int)blockIdx.x);
+    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + (D / 64) * 2048 + 8192 <= 163840;
+    dec2_body<D, R, WAVES, STAGES, QBF16, AFF, false, SQ>(p, s_stage, (int)blockIdx.x);
 }
 
 // Decode that appends the step's new token itself (four waves, two stages,
@@ -556,7 +584,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
 template <int D, int R, bool QBF16>
 __global__ __launch_bounds__(256) void attn_dec2_append_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, false>()];
-    dec2_body<D, R, 4, 2, QBF16, false, true>(p, s_stage, (int)blockIdx.x);
+    dec2_body<D, R, 4, 2, QBF16, false, true, true>(p, s_stage, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
