@@ -367,6 +367,11 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
     for (int a = 0; a < NA; ++a) grp[a] = ((16 * a + n16) / R) % NG;
 
+    // Every path has consumed the page-id load by now; an explicit use says so.
+    // Otherwise the compiler's own wait for that load (on the paths that
+    // issued no first copy) lands at the top of each iteration, where its
+    // vmcnt(0) also drains the copies in flight and breaks the prefetch.
+    asm volatile("" ::"v"(my_id));
     for (int t = 0; t < nt; ++t) {
         const int slot = t % STAGES;
         if (t + STAGES - 1 < nt) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
@@ -810,6 +815,11 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
         for (int dt = 0; dt < NDT; ++dt) acc[rb][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
+    // Every path has consumed the page-id load by now; an explicit use says so.
+    // Otherwise the compiler's own wait for that load (on the paths that
+    // issued no first copy) lands at the top of each iteration, where its
+    // vmcnt(0) also drains the copies in flight and breaks the prefetch.
+    asm volatile("" ::"v"(my_id));
     for (int t = 0; t < nt; ++t) {
         const int slot = t % STAGES;
         if (t + STAGES - 1 < nt) issue(t + STAGES - 1, (t + STAGES - 1) % STAGES);
