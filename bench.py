@@ -70,8 +70,7 @@ def parse():
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the sharding design is described in DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}))
         return 2
     if args.cpu_report:
         return cpu_report()
