@@ -9,10 +9,11 @@
 // n_draft drafts) the service cost of a configuration c is
 //     cost(c) = sum over the unit's two shapes p of median(c, p) / median(default, p)
 // with shapes at ctx_small and ctx_large, term weights 1, one launch per
-// layer-step.  Medians are over single launches bracketed by HIP events on
-// the tuner's own stream; launches rotate over distinct cache copies (and,
-// for the small context, over disjoint page sets) whose total exceeds four
-// times the 256 MiB last-level cache, so every launch streams from HBM.
+// layer-step.  Times are per launch within a replayed graph of launches on
+// the tuner's own stream (medians over replays, bracketed by HIP events);
+// the launches rotate over distinct cache copies (and, for the small
+// context, over disjoint page sets) whose total exceeds four times the
+// 256 MiB last-level cache, so every launch streams from HBM.
 //
 // Order: each unit's default first; then one candidate at a time from the
 // unit with the earliest virtual completion time
@@ -222,7 +223,6 @@ class Tuner {
     int hq_ = 0, h_ = 0, d_ = 0, w_ = 0, g_ = 0;
     float scale_ = 0;
     int pages_ = 0, small_pages_ = 0, n_copies_ = 0, n_sets_ = 0, reps_ = 0;
-    uint64_t rot_ = 0;                   // rolling rotation counter
     size_t cache_bytes_ = 0;
     std::vector<q8k4v_cache> copies_;
     int32_t* d_tables_ = nullptr;        // [n_sets][pages]: set 0 is the full permutation
@@ -360,7 +360,7 @@ int32_t Tuner::setup(std::string* why) {
     // the fused combine's counters start at zero and reset themselves
     if (hipMemsetAsync(d_ws_, 0, ws_bytes_, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
     if (hipStreamSynchronize(stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: synthesis");
-    reps_ = 24;
+    reps_ = 5;
     events_.resize(2 * reps_);
     for (auto& e : events_)
         if (hipEventCreate(&e) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: events");
@@ -378,29 +378,44 @@ int32_t Tuner::launch(const q8k4v_config* cfg, const Shape& s, int copy, int set
 }
 
 int32_t Tuner::time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us) {
-    // two untimed launches, then reps_ single launches, each on the next copy
-    // copies are taken in a rolling order across all measurements, so a copy
-    // comes back only after every other copy (> 4x the LLC) has been read
-    for (int r = 0; r < 2; ++r) {
-        const int32_t rc = launch(cfg, s, (int)(rot_++ % n_copies_), 0, d_out_, d_q_);
-        if (rc != Q8K4V_OK) return rc;
+    // One captured graph of launches that rotate over the cache copies (and,
+    // for the small shape, over the disjoint page sets), so every replay
+    // streams more than 4x the LLC from HBM and no copy is re-read within a
+    // replay or across the seam between two.  Replaying a graph is how a
+    // serving loop issues these launches (no host launch gap between them);
+    // the time per launch is a replay's time over its launches, the median
+    // over reps_ timed replays after one untimed.
+    const int G = s.small ? n_copies_ * n_sets_ : n_copies_;
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(stream_, hipStreamCaptureModeThreadLocal) != hipSuccess)
+        return hip_fail(hipGetLastError(), "tune_select: begin capture");
+    int32_t rc = Q8K4V_OK;
+    for (int r = 0; r < G && rc == Q8K4V_OK; ++r)
+        rc = launch(cfg, s, r % n_copies_, s.small ? (r / n_copies_) % n_sets_ : 0, d_out_, d_q_);
+    const hipError_t ec = hipStreamEndCapture(stream_, &graph);
+    if (rc != Q8K4V_OK || ec != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc != Q8K4V_OK ? rc : hip_fail(ec, "tune_select: capture");
     }
-    for (int r = 0; r < reps_; ++r) {
-        const uint64_t k = rot_++;
-        const int copy = (int)(k % n_copies_);
-        const int set = s.small ? (int)((k / n_copies_) % n_sets_) : 0;
-        if (hipEventRecord(events_[2 * r], stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: event");
-        const int32_t rc = launch(cfg, s, copy, set, d_out_, d_q_);
-        if (rc != Q8K4V_OK) return rc;
-        if (hipEventRecord(events_[2 * r + 1], stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: event");
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return hip_fail(ei, "tune_select: graph instantiate");
+    hipError_t e = hipGraphLaunch(exec, stream_);
+    for (int r = 0; r < reps_ && e == hipSuccess; ++r) {
+        e = hipEventRecord(events_[2 * r], stream_);
+        if (e == hipSuccess) e = hipGraphLaunch(exec, stream_);
+        if (e == hipSuccess) e = hipEventRecord(events_[2 * r + 1], stream_);
     }
-    if (hipStreamSynchronize(stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: timing");
+    if (e == hipSuccess) e = hipStreamSynchronize(stream_);
+    (void)hipGraphExecDestroy(exec);
+    if (e != hipSuccess) return hip_fail(e, "tune_select: timing");
     std::vector<double> t(reps_);
     for (int r = 0; r < reps_; ++r) {
         float ms = 0;
         if (hipEventElapsedTime(&ms, events_[2 * r], events_[2 * r + 1]) != hipSuccess)
             return hip_fail(hipGetLastError(), "tune_select: elapsed");
-        t[r] = ms * 1e3;
+        t[r] = ms * 1e3 / G;
     }
     std::nth_element(t.begin(), t.begin() + reps_ / 2, t.end());
     *median_us = t[reps_ / 2];
@@ -823,7 +838,8 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     if (!why.empty()) j += ",\"error\":\"" + why + "\"";
     j += ",\"rotation\":{\"copies\":" + std::to_string(n_copies_) + ",\"copy_bytes\":" + std::to_string(cache_bytes_) +
          ",\"small_page_sets\":" + std::to_string(n_sets_) + ",\"llc_multiple\":" +
-         fmt((double)n_copies_ * cache_bytes_ / (double)kLlcBytes) + ",\"launches_per_median\":" + std::to_string(reps_) + "}";
+         fmt((double)n_copies_ * cache_bytes_ / (double)kLlcBytes) + ",\"timed_replays\":" + std::to_string(reps_) + ",\"launches_per_replay\":[" +
+         std::to_string(n_copies_ * n_sets_) + "," + std::to_string(n_copies_) + "]}";
     if (!setup_note_.empty()) j += ",\"note\":\"" + setup_note_ + "\"";
     j += ",\"installed\":" + std::string(install ? "true" : "false");
     j += ",\"identity\":\"" + identity + "\",\"identity_hash\":\"" + id_hash + "\"";
