@@ -134,8 +134,19 @@ def _stream(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
-def _ptr(t) -> C.c_void_p:
-    return C.c_void_p(t.data_ptr()) if t is not None else C.c_void_p(0)
+def _ptr(t, name: str = "tensor", i32: bool = False) -> C.c_void_p:
+    """Device pointer of a tensor argument: the library reads it as a dense
+    array on the current device, so it must be a contiguous device tensor
+    (int32 for lengths, positions and page tables)."""
+    if t is None:
+        return C.c_void_p(0)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if i32 and t.dtype != _torch().int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    return C.c_void_p(t.data_ptr())
 
 
 def _dtype_code(t) -> int:
@@ -209,8 +220,8 @@ def kv_quant_append(cache: PagedKVCache, k_new, v_new, cu_new, start_pos, page_t
     if total_new is None:
         total_new = int(k_new.shape[0])
     n_seqs = int(start_pos.shape[0])
-    rc = lib.kv_quant_append(C.byref(cache.desc), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(cu_new),
-                             _ptr(start_pos), _ptr(page_table), int(page_table.shape[1]), n_seqs,
+    rc = lib.kv_quant_append(C.byref(cache.desc), _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _dtype_code(k_new), _ptr(cu_new, "cu_new", i32=True),
+                             _ptr(start_pos, "start_pos", i32=True), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]), n_seqs,
                              int(total_new), _stream(stream))
     _check("kv_quant_append", rc)
 
@@ -240,10 +251,10 @@ def attn_decode_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_t
         softmax_scale = 1.0 / math.sqrt(D)
     if workspace is None:
         workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, 0, cfg), q.device)
-    rc = lib.attn_decode_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq, _ptr(seq_lens),
-                               int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+    rc = lib.attn_decode_q8k4v(C.byref(cache.desc), _ptr(q, "q"), _dtype_code(q), _ptr(out, "out"), B, Hq, _ptr(seq_lens, "seq_lens", i32=True),
+                               int(max_seq_len), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
                                float(softmax_scale), C.byref(cfg) if cfg is not None else None,
-                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+                               _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("attn_decode_q8k4v", rc)
     return out
 
@@ -271,11 +282,11 @@ def attn_decode_prefix_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int,
     if workspace is None:
         workspace = _workspace(prefix_workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len,
                                                       n_prefix_pages, cfg), q.device)
-    rc = lib.attn_decode_prefix_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq,
-                                      _ptr(seq_lens), int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+    rc = lib.attn_decode_prefix_q8k4v(C.byref(cache.desc), _ptr(q, "q"), _dtype_code(q), _ptr(out, "out"), B, Hq,
+                                      _ptr(seq_lens, "seq_lens", i32=True), int(max_seq_len), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
                                       int(n_prefix_pages), float(softmax_scale),
                                       C.byref(cfg) if cfg is not None else None,
-                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+                                      _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("attn_decode_prefix_q8k4v", rc)
     return out
 
@@ -295,10 +306,10 @@ def attn_decode_append_q8k4v(cache: PagedKVCache, k_new, v_new, q, seq_lens, max
         softmax_scale = 1.0 / math.sqrt(D)
     if workspace is None:
         workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, 0, cfg), q.device)
-    rc = lib.attn_decode_append_q8k4v(C.byref(cache.desc), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q),
-                                      _dtype_code(q), _ptr(out), B, Hq, _ptr(seq_lens), int(max_seq_len),
-                                      _ptr(page_table), int(page_table.shape[1]), float(softmax_scale),
-                                      C.byref(cfg) if cfg is not None else None, _ptr(workspace),
+    rc = lib.attn_decode_append_q8k4v(C.byref(cache.desc), _ptr(k_new, "k_new"), _ptr(v_new, "v_new"), _dtype_code(k_new), _ptr(q, "q"),
+                                      _dtype_code(q), _ptr(out, "out"), B, Hq, _ptr(seq_lens, "seq_lens", i32=True), int(max_seq_len),
+                                      _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]), float(softmax_scale),
+                                      C.byref(cfg) if cfg is not None else None, _ptr(workspace, "workspace"),
                                       workspace.numel() * workspace.element_size(), _stream(stream))
     _check("attn_decode_append_q8k4v", rc)
     return out
@@ -319,10 +330,10 @@ def attn_prefill_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_
         softmax_scale = 1.0 / math.sqrt(D)
     if workspace is None:
         workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, Wn, cfg), q.device)
-    rc = lib.attn_prefill_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq, Wn,
-                                _ptr(seq_lens), int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+    rc = lib.attn_prefill_q8k4v(C.byref(cache.desc), _ptr(q, "q"), _dtype_code(q), _ptr(out, "out"), B, Hq, Wn,
+                                _ptr(seq_lens, "seq_lens", i32=True), int(max_seq_len), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
                                 float(softmax_scale), C.byref(cfg) if cfg is not None else None,
-                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+                                _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("attn_prefill_q8k4v", rc)
     return out
 
@@ -341,10 +352,10 @@ def attn_verify_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_t
         softmax_scale = 1.0 / math.sqrt(D)
     if workspace is None:
         workspace = _workspace(workspace_bytes(B, Hq, cache.num_kv_heads, D, max_seq_len, Wd, cfg), q.device)
-    rc = lib.attn_verify_q8k4v(C.byref(cache.desc), _ptr(q), _dtype_code(q), _ptr(out), B, Hq, Wd,
-                               _ptr(seq_lens), int(max_seq_len), _ptr(page_table), int(page_table.shape[1]),
+    rc = lib.attn_verify_q8k4v(C.byref(cache.desc), _ptr(q, "q"), _dtype_code(q), _ptr(out, "out"), B, Hq, Wd,
+                               _ptr(seq_lens, "seq_lens", i32=True), int(max_seq_len), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
                                float(softmax_scale), C.byref(cfg) if cfg is not None else None,
-                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+                               _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("attn_verify_q8k4v", rc)
     return out
 

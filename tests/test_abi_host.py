@@ -165,3 +165,15 @@ def test_tuner_rejects_bad_requests(lib):
     assert tune(ctx_small=0) == -1
     assert tune(ctx_small=8192, ctx_large=4096) == -1
     assert lib.tune_select(None, None, None, 0) == -1
+
+
+def test_binding_rejects_host_tensors():
+    """The binding hands raw device pointers to the library: host tensors are
+    refused before any call (no CPU path)."""
+    import torch
+    import decode_attention_quantized_kv_amd as q8
+    with pytest.raises(ValueError):
+        q8._ptr(torch.zeros(4), "q")
+    with pytest.raises(ValueError):
+        q8._ptr(torch.zeros(4, dtype=torch.int32), "seq_lens", i32=True)
+    assert q8._ptr(None).value is None
