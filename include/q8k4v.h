@@ -327,9 +327,11 @@ int32_t attn_prefill_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dt
  * (term weights 1, one launch per layer-step).  Every step -- allocation,
  * input synthesis, the defaults' measurement, the candidates, the gate --
  * runs inside the wall-clock budget (at most 60 s); a candidate not measured
- * before the deadline is "unknown" and never admitted.  Timing rotates over
- * distinct cache copies whose total size exceeds 4 x 256 MiB (the MI355X
- * last-level cache), so no pass is served from a warm cache.  Admission
+ * before the deadline is "unknown" and never admitted.  A time is per
+ * launch inside a captured graph of launches replayed on the tuner's own
+ * stream (median over the timed replays); the launches rotate over distinct
+ * cache copies whose total size exceeds 4 x 256 MiB (the MI355X last-level
+ * cache), so no launch is served from a warm cache.  Admission
  * (section 4 of the same page, alpha = 8): on every checked output the
  * candidate's deviation from the default configuration's output must not
  * exceed alpha times the storage-resolution noise, i.e. the change of the
