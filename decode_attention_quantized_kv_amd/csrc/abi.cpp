@@ -224,7 +224,23 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);
     }
     sp = std::max(sp, unit);
-    if (kernel == kDec2 || kernel == kRows) sp = std::min(sp, 64 * cfg.waves_per_wg);   // <= 64 pages per wave
+    if ((kernel == kDec2 || kernel == kRows) && sp > 64 * cfg.waves_per_wg) {
+        // a wave's page ids sit one per lane: at most 64 pages per wave.  With
+        // the automatic split, the extra splits this forces take the grid to
+        // the next whole number of workgroups per CU (an even grid) instead of
+        // just over one
+        const int32_t cap = 64 * cfg.waves_per_wg;
+        if (cfg.split_pages > 0) {
+            sp = cap;
+        } else {
+            const int64_t cus = device_cu_count();
+            const int64_t per = (int64_t)a.n_seqs * H * plan->row_chunks;
+            const int64_t need = (max_np + cap - 1) / cap;                 // splits at the cap
+            const int64_t k = (need * per + cus - 1) / cus;                // workgroups per CU
+            const int64_t splits = std::max<int64_t>(need, (k * cus + per - 1) / per);
+            sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);   // <= cap: unit divides cap
+        }
+    }
     plan->split_pages = sp;
     plan->n_splits = (max_np + sp - 1) / sp;
     if (plan->n_splits > kCombineMaxSplits) {   // the combine holds one weight per split in LDS
