@@ -226,18 +226,23 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     sp = std::max(sp, unit);
     if ((kernel == kDec2 || kernel == kRows) && sp > 64 * cfg.waves_per_wg) {
         // a wave's page ids sit one per lane: at most 64 pages per wave.  With
-        // the automatic split, the extra splits this forces take the grid to
-        // the next whole number of workgroups per CU (an even grid) instead of
-        // just over one
+        // the automatic split of a one-chunk query block (decode, small
+        // verify), the extra splits this forces are made even: a multiple of
+        // 8 (splits are dealt round robin over the 8 XCDs, so every XCD gets
+        // the same pages), then at least the next whole number of workgroups
+        // per CU (not just over one).  Blocks of many row chunks (prefill)
+        // keep the capped split: their workgroups are many already, and
+        // doubling them costs more in per-workgroup set-up than the uneven
+        // last split (measured)
         const int32_t cap = 64 * cfg.waves_per_wg;
-        if (cfg.split_pages > 0) {
+        if (cfg.split_pages > 0 || plan->row_chunks > 1) {
             sp = cap;
         } else {
             const int64_t cus = device_cu_count();
             const int64_t per = (int64_t)a.n_seqs * H * plan->row_chunks;
-            const int64_t need = (max_np + cap - 1) / cap;                 // splits at the cap
-            const int64_t k = (need * per + cus - 1) / cus;                // workgroups per CU
-            const int64_t splits = std::max<int64_t>(need, (k * cus + per - 1) / per);
+            int64_t splits = round_up((int32_t)((max_np + cap - 1) / cap), 8);   // splits at the cap, even over XCDs
+            const int64_t k = (splits * per + cus - 1) / cus;                       // workgroups per CU
+            splits = round_up((int32_t)std::max<int64_t>(splits, (k * cus + per - 1) / per), 8);
             sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);   // <= cap: unit divides cap
         }
     }
