@@ -269,11 +269,12 @@ __global__ __launch_bounds__(256) void append_pages_kernel(Q8K4V_APPEND_PARAMS) 
 int32_t launch_append(const AppendArgs& a, hipStream_t stream) {
     const q8k4v_cache& c = *a.cache;
     if (a.total_new == 0) return Q8K4V_OK;
-    // one token per sequence (the decode step): a wavefront per (token, head);
-    // otherwise a workgroup per (16 new tokens, head), whole pages at once --
-    // its vector loads and stores want 16-byte aligned inputs and pools
+    // bulk calls (prompts, chunks: 256 new tokens or more) take a workgroup
+    // per (16 new tokens, head), whole pages at once -- its vector loads and
+    // stores want 16-byte aligned inputs and pools; small calls (decode steps,
+    // drafts) a wavefront per (token, head), the most parallel mapping
     const uintptr_t al = (uintptr_t)a.k_new | (uintptr_t)a.v_new | (uintptr_t)c.k_codes | (uintptr_t)c.v_codes;
-    const bool pages = a.last_of == nullptr && (al & 15) == 0;
+    const bool pages = a.last_of == nullptr && (al & 15) == 0 && a.total_new >= 256;
     const long items = (long)a.total_new * c.num_kv_heads;
     const long blocks = pages ? (long)((a.total_new + 15) / 16) * c.num_kv_heads : (items + 3) / 4;
     if (blocks > 0x7FFFFFFFL) return fail(Q8K4V_EINVAL, "kv_quant_append: too many tokens in one call");

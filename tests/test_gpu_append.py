@@ -63,6 +63,26 @@ def test_ragged_batches_odd_starts(D, dtype):
     _assert_same(w, cache_to_host(upload_cache(w)), oracle_cache(w))
 
 
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f32")])
+def test_bulk_calls_mixed_chunks(D, dtype):
+    """Calls of 256 tokens or more take the page-block kernel: one ragged call
+    (sequences of 0..250 tokens from position 0: chunks that fill one page of
+    one sequence and chunks that straddle sequences or pages), then longer
+    sequences appended in two calls cut at random positions (odd starts)."""
+    from tests.gpu_util import cache_to_host, upload_cache
+    w = workloads.build("bulk_ragged", seed=41, num_q_heads=8, num_kv_heads=2, head_dim=D, dtype=dtype,
+                        seq_lens=[1, 15, 16, 17, 33, 250, 0, 61], outliers=True)
+    assert sum(len(a.k) for a in w.appends) >= 256
+    print(f"[append] bulk ragged one call D={D} {dtype}", flush=True)
+    _assert_same(w, cache_to_host(upload_cache(w)), oracle_cache(w))
+    rng = np.random.default_rng(D)
+    w = workloads.build("bulk_cut", seed=42, num_q_heads=8, num_kv_heads=2, head_dim=D, dtype=dtype,
+                        seq_lens=[700, 333], outliers=True, spare_pages=2)
+    w = _resplit(w, rng, pieces=2)
+    print(f"[append] bulk two calls D={D} {dtype}: {[len(a.k) for a in w.appends]}", flush=True)
+    _assert_same(w, cache_to_host(upload_cache(w)), oracle_cache(w))
+
+
 def _edge_rows(D):
     rows = []
     z = np.zeros(D, np.float32)
