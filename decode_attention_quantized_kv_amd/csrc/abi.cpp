@@ -371,7 +371,7 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     // 8 waves for a large prefix block on its own; 4 when it shares the
     // launch with a four-wave, two-stage replicated-row suffix pass
     const bool fuse = rows > 16 && sp.kernel == kDec2 && (sp.rows == 4 || sp.rows == 8) && sp.waves == 4 &&
-                      sp.stages == 2 && a.cache->codec == Q8K4V_CODEC_SYMMETRIC;
+                      sp.stages == 2;
     pp.waves = (rows > 16 && !fuse) ? 8 : 4;
     pp.stages = 2;
     pp.rows_per_wg = rows > 16 ? 32 : 16;
@@ -422,7 +422,7 @@ int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp,
     suf.fused = 0;
 
     int32_t rc;
-    if (cascade_fusable(cp.pre, cp.suf) && !pre.affine) {
+    if (cascade_fusable(cp.pre, cp.suf)) {
         rc = launch_cascade_fused(pre, suf, D, bf, cp.suf.rows, stream);
         if (rc != Q8K4V_OK) return rc;
     } else {
@@ -521,8 +521,8 @@ size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t
         return q8k4v_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 0, cfg);
     q8k4v_config dflt;
     cfg = cascade_config(cfg, num_q_heads, num_kv_heads, &dflt);
-    // the prefix plan depends on the codec (only a symmetric cache fuses the
-    // two passes): the larger need of the codecs the configuration supports
+    // the larger need of the codecs the configuration supports (a plan
+    // unavailable for one codec does not count)
     size_t need = 0;
     const std::string saved = g_last_error;
     for (int32_t codec : {Q8K4V_CODEC_SYMMETRIC, Q8K4V_CODEC_AFFINE}) {

@@ -1088,11 +1088,11 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
 // one tile ring per workgroup.  Both are four-wave, two-stage rings, so a
 // compute-bound prefix workgroup and memory-bound suffix workgroups share
 // each CU.  pre_blocks is a multiple of 8, which keeps every block's XCD.
-template <int D, int R, bool QBF16>
+template <int D, int R, bool QBF16, bool AFF>
 __global__ __launch_bounds__(256) void attn_cascade_kernel(const AttnParams pre, const AttnParams suf, int pre_blocks) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D>()];
-    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16, false>(pre, s_stage, (int)blockIdx.x);
-    else dec2_body<D, R, 4, 2, QBF16, false>(suf, s_stage, (int)blockIdx.x - pre_blocks);
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, AFF>()];
+    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16, AFF>(pre, s_stage, (int)blockIdx.x);
+    else dec2_body<D, R, 4, 2, QBF16, AFF>(suf, s_stage, (int)blockIdx.x - pre_blocks);
 }
 
 template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
@@ -1160,22 +1160,22 @@ LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
     return nullptr;
 }
 
-template <int D, int R, bool QBF16>
+template <int D, int R, bool QBF16, bool AFF>
 hipError_t launch_cascade_t(const AttnParams& pre, const AttnParams& suf, hipStream_t stream) {
     const int pre_total = pre.n_seqs * pre.H * pre.n_splits * pre.row_chunks;
     const int pre_blocks = 8 * ((pre_total + 7) / 8);
     const int suf_total = suf.n_seqs * suf.H * suf.n_splits * suf.row_chunks;
     const int suf_blocks = 8 * ((suf_total + 7) / 8);
-    hipLaunchKernelGGL((attn_cascade_kernel<D, R, QBF16>), dim3(pre_blocks + suf_blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((attn_cascade_kernel<D, R, QBF16, AFF>), dim3(pre_blocks + suf_blocks), dim3(256), 0, stream,
                        pre, suf, pre_blocks);
     return hipGetLastError();
 }
 
-template <int D, bool QBF16>
+template <int D, bool QBF16, bool AFF>
 hipError_t pick_cascade(int rows, const AttnParams& pre, const AttnParams& suf, hipStream_t stream) {
     switch (rows) {
-        case 4: return launch_cascade_t<D, 4, QBF16>(pre, suf, stream);
-        case 8: return launch_cascade_t<D, 8, QBF16>(pre, suf, stream);
+        case 4: return launch_cascade_t<D, 4, QBF16, AFF>(pre, suf, stream);
+        case 8: return launch_cascade_t<D, 8, QBF16, AFF>(pre, suf, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1228,8 +1228,13 @@ bool cascade_fusable(const Plan& pre, const Plan& suf) {
 int32_t launch_cascade_fused(const AttnParams& pre, const AttnParams& suf, int head_dim, bool qbf16, int rows,
                              hipStream_t stream) {
     hipError_t e;
-    if (head_dim == 128) e = qbf16 ? pick_cascade<128, true>(rows, pre, suf, stream) : pick_cascade<128, false>(rows, pre, suf, stream);
-    else e = qbf16 ? pick_cascade<64, true>(rows, pre, suf, stream) : pick_cascade<64, false>(rows, pre, suf, stream);
+    if (pre.affine) {
+        if (head_dim == 128) e = qbf16 ? pick_cascade<128, true, true>(rows, pre, suf, stream) : pick_cascade<128, false, true>(rows, pre, suf, stream);
+        else e = qbf16 ? pick_cascade<64, true, true>(rows, pre, suf, stream) : pick_cascade<64, false, true>(rows, pre, suf, stream);
+    } else {
+        if (head_dim == 128) e = qbf16 ? pick_cascade<128, true, false>(rows, pre, suf, stream) : pick_cascade<128, false, false>(rows, pre, suf, stream);
+        else e = qbf16 ? pick_cascade<64, true, false>(rows, pre, suf, stream) : pick_cascade<64, false, false>(rows, pre, suf, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
     return Q8K4V_OK;
 }
