@@ -343,18 +343,31 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
         coef = s_coef[lane];
         qsum = s_qsum[lane];
     }
-    // APP: codes and scales of the new token (symmetric codec)
+    // APP: codes and scales (affine: and zero points) of the new token, by
+    // the append kernel's rule; affine key codes and zero point are stored
+    // XOR 0x80 as there
     int app_kc[EPL] = {}, app_vc[EPL] = {};
     _Float16 app_ks16 = 0, app_vs16 = 0;
+    int app_kz = 0, app_vz = 0;
     if (APP && app_owner) {
-        float ka = 0.0f;
+        if (AFF) {
+            float mn = app_kx[0], mx = app_kx[0];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) ka = fmaxf(ka, fabsf(app_kx[e]));
-        app_ks16 = scale_of(wave_max(ka, 64), 127.0f);
+            for (int e = 1; e < EPL; ++e) { mn = fminf(mn, app_kx[e]); mx = fmaxf(mx, app_kx[e]); }
+            const Affine a = affine_of(wave_min(mn, 64), wave_max(mx, 64), 255.0f);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) app_kc[e] = code_of(app_kx[e], (float)app_ks16, 127.0f);
-        int z;
-        value_codes<EPL, 32 / EPL, false>(app_vx, app_vc, &app_vs16, &z);
+            for (int e = 0; e < EPL; ++e) app_kc[e] = affine_code(app_kx[e], a, 255.0f) ^ 0x80;
+            app_ks16 = a.s16;
+            app_kz = (int)a.z ^ 0x80;
+        } else {
+            float ka = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) ka = fmaxf(ka, fabsf(app_kx[e]));
+            app_ks16 = scale_of(wave_max(ka, 64), 127.0f);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) app_kc[e] = code_of(app_kx[e], (float)app_ks16, 127.0f);
+        }
+        value_codes<EPL, 32 / EPL, AFF>(app_vx, app_vc, &app_vs16, &app_vz);
     }
     const int lim_min = w.L - p.W + 1;         // every row sees the positions below this
 
@@ -402,11 +415,19 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
             if (lane == 0) {
                 *(uint16_t*)(sw + OFF_KS + app_u * KSB + app_slot * 2) = ksb;
                 const_cast<uint16_t*>(p.k_scales)[blk * 16 + app_slot] = ksb;
+                if (AFF) {
+                    sw[OFF_KZ + app_u * KZB + app_slot] = (uint8_t)app_kz;
+                    const_cast<int8_t*>(p.k_zeros)[blk * 16 + app_slot] = (int8_t)app_kz;
+                }
             }
             if (lane % (32 / EPL) == 0) {
                 const int g = lane / (32 / EPL);
                 *(uint16_t*)(sw + OFF_VS + app_u * VSB + (app_slot * NG + g) * 2) = vsb;
                 const_cast<uint16_t*>(p.v_scales)[(blk * 16 + app_slot) * NG + g] = vsb;
+                if (AFF) {
+                    sw[OFF_VZ + app_u * VZB + app_slot * NG + g] = (uint8_t)app_vz;
+                    const_cast<uint8_t*>(p.v_zeros)[(blk * 16 + app_slot) * NG + g] = (uint8_t)app_vz;
+                }
             }
         }
         // ---- tile to registers
@@ -584,12 +605,11 @@ __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams 
     dec2_body<D, R, WAVES, STAGES, QBF16, AFF, false, SQ>(p, s_stage, (int)blockIdx.x);
 }
 
-// Decode that appends the step's new token itself (four waves, two stages,
-// symmetric codec).
-template <int D, int R, bool QBF16>
+// Decode that appends the step's new token itself (four waves, two stages).
+template <int D, int R, bool QBF16, bool AFF>
 __global__ __launch_bounds__(256) void attn_dec2_append_kernel(const AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, false>()];
-    dec2_body<D, R, 4, 2, QBF16, false, true, true>(p, s_stage, (int)blockIdx.x);
+    __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, AFF>()];
+    dec2_body<D, R, 4, 2, QBF16, AFF, true, true>(p, s_stage, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1180,22 +1200,22 @@ hipError_t pick_cascade(int rows, const AttnParams& pre, const AttnParams& suf, 
     }
 }
 
-template <int D, int R, bool QBF16>
+template <int D, int R, bool QBF16, bool AFF>
 hipError_t launch_append_t(const AttnParams& kp, hipStream_t stream) {
     const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
     const int blocks = 8 * ((total + 7) / 8);
-    hipLaunchKernelGGL((attn_dec2_append_kernel<D, R, QBF16>), dim3(blocks), dim3(256), 0, stream, kp);
+    hipLaunchKernelGGL((attn_dec2_append_kernel<D, R, QBF16, AFF>), dim3(blocks), dim3(256), 0, stream, kp);
     return hipGetLastError();
 }
 
-template <int D, bool QBF16>
+template <int D, bool QBF16, bool AFF>
 LaunchFn pick_append(int rows) {
     switch (rows) {
-        case 1: return &launch_append_t<D, 1, QBF16>;
-        case 2: return &launch_append_t<D, 2, QBF16>;
-        case 4: return &launch_append_t<D, 4, QBF16>;
-        case 8: return &launch_append_t<D, 8, QBF16>;
-        case 16: return &launch_append_t<D, 16, QBF16>;
+        case 1: return &launch_append_t<D, 1, QBF16, AFF>;
+        case 2: return &launch_append_t<D, 2, QBF16, AFF>;
+        case 4: return &launch_append_t<D, 4, QBF16, AFF>;
+        case 8: return &launch_append_t<D, 8, QBF16, AFF>;
+        case 16: return &launch_append_t<D, 16, QBF16, AFF>;
         default: return nullptr;
     }
 }
@@ -1203,15 +1223,21 @@ LaunchFn pick_append(int rows) {
 }  // namespace
 
 // Decode with the step's token appended in the same launch: replicated-row
-// plan with four waves and two stages on a symmetric cache.
+// plan with four waves and two stages (either codec).
 bool decode_append_fusable(const Plan& plan, const q8k4v_cache& c) {
-    return plan.kernel == kDec2 && plan.waves == 4 && plan.stages == 2 && c.codec == Q8K4V_CODEC_SYMMETRIC;
+    (void)c;
+    return plan.kernel == kDec2 && plan.waves == 4 && plan.stages == 2;
 }
 
 int32_t launch_dec2_append(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream) {
     LaunchFn fn;
-    if (head_dim == 128) fn = qbf16 ? pick_append<128, true>(plan.rows) : pick_append<128, false>(plan.rows);
-    else fn = qbf16 ? pick_append<64, true>(plan.rows) : pick_append<64, false>(plan.rows);
+    if (kp.affine) {
+        if (head_dim == 128) fn = qbf16 ? pick_append<128, true, true>(plan.rows) : pick_append<128, false, true>(plan.rows);
+        else fn = qbf16 ? pick_append<64, true, true>(plan.rows) : pick_append<64, false, true>(plan.rows);
+    } else {
+        if (head_dim == 128) fn = qbf16 ? pick_append<128, true, false>(plan.rows) : pick_append<128, false, false>(plan.rows);
+        else fn = qbf16 ? pick_append<64, true, false>(plan.rows) : pick_append<64, false, false>(plan.rows);
+    }
     if (!fn) return fail(Q8K4V_EUNSUPPORTED, "attention: no appending decode kernel for this row count");
     const hipError_t e = fn(kp, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

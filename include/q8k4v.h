@@ -277,7 +277,7 @@ int32_t attn_verify_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
  * puts it into its LDS copy of the page before the tile is read, and writes
  * it to the cache for later calls (blog.123qwe.co.kr/?p=3927, section 5:
  * the decode unit over the k8v4 cache).  Fused when the decode plan is the
- * replicated-row kernel with 4 waves and 2 stages on a symmetric cache (the
+ * replicated-row kernel with 4 waves and 2 stages, with either codec (the
  * defaults for 1, 2, 4, 8 or 16 rows per kv head); otherwise the append
  * kernel runs first, then the decode.
  *

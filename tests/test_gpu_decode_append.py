@@ -30,14 +30,14 @@ def _split_last(w):
     return w.appends[:-1] + [head], last.k[rows], last.v[rows]
 
 
-def _run(w, cfg):
+def _run(w, cfg, codec="symmetric"):
     import torch
     import decode_attention_quantized_kv_amd as q8
     from tests.gpu_util import cache_to_host, to_dev, upload_cache
-    full = upload_cache(w)                                 # the append kernel, every token
+    full = upload_cache(w, codec=codec)                    # the append kernel, every token
     appends, k_last, v_last = _split_last(w)
     w_step = workloads.Workload(**{**w.__dict__, "appends": appends})
-    cache = upload_cache(w_step)
+    cache = upload_cache(w_step, codec=codec)
     c = None if cfg is None else q8.make_config(**cfg)
     q, lens, pt = to_dev(w.q, w.dtype), to_dev(w.seq_lens), to_dev(w.page_table)
     msl = int(w.seq_lens.max())
@@ -74,6 +74,22 @@ def test_groups_heads_dtypes(hq, hkv, D, dt):
     got, sep = _run(w, None)
     assert np.array_equal(got, sep)
     assert normalized_err(w, got, oracle_out(w)) <= ATOL_SIGMA
+
+
+@pytest.mark.parametrize("hq,hkv,D,dt,cfg", [(32, 8, 128, "bf16", None), (8, 8, 64, "f32", None),
+                                             (32, 8, 128, "bf16", dict(variant=4, waves_per_wg=8))], ids=str)
+def test_affine_cache(hq, hkv, D, dt, cfg):
+    """Affine codec: the fused step writes the token's codes, scales and zero
+    points as kv_quant_append does (bit for bit), and its output equals the
+    separate append + decode and the oracle over the affine cache."""
+    from tests.util import oracle_cache
+    w = workloads.build("dec_app_aff", seed=140 + D, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, dtype=dt,
+                        seq_lens=[1, 2, 16, 17, 33, 700], outliers=True)
+    got, sep = _run(w, cfg, codec="affine")
+    assert np.array_equal(got, sep), cfg
+    err = normalized_err(w, got, oracle_out(w, oracle_cache(w, codec_name="affine")))
+    print(f"[decode_append] affine hq={hq} D={D} {dt} cfg {cfg}: {err:.3e}", flush=True)
+    assert err <= ATOL_SIGMA, err
 
 
 def test_graph_replays_rewrite_the_same_token():
