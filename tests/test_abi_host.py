@@ -177,3 +177,22 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         q8._ptr(torch.zeros(4, dtype=torch.int32), "seq_lens", i32=True)
     assert q8._ptr(None).value is None
+
+
+def test_long_context_splits_are_even(lib):
+    """Beyond the 64-pages-per-wave cap, a one-chunk decode takes a whole
+    number of workgroups per CU and a multiple of 8 splits (the workspace
+    holds one (m, l, o[D]) record per split, kv head and row); prefill blocks
+    keep the capped split."""
+    import decode_attention_quantized_kv_amd as q8
+    rec = 4 * (128 + 4)
+
+    def splits(ctx, n_new=0):
+        rows = 4 * max(1, n_new)
+        return q8.workspace_bytes(1, 32, 8, 128, ctx, n_new) / (8 * rows * rec)
+
+    assert splits(65536) == 32 and splits(131072) == 32       # under the cap: one workgroup per CU
+    for ctx in (163840, 200000, 262144):
+        s = splits(ctx)
+        assert s == 64, (ctx, s)                             # two per CU, 8 per XCD
+    assert splits(65536 + 512, 512) == 16                    # 9 capped splits, padded to 16
