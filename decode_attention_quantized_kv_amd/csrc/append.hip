@@ -183,9 +183,9 @@ Q8K4V_DEV void load_seg(const void* base, size_t row, int u, float (&x)[EPT]) {
 // -- and write it whole: key rows as contiguous 4- or 8-byte stores, the
 // value nibble pairs (slots 2j, 2j+1 of one dimension) transposed through
 // LDS into the dimension-major rows and written as one contiguous block.  The
-// scales and codes are those of the per-token path (same reductions, same
-// device functions).  Any other chunk, and every chunk of an affine cache,
-// runs the per-token path, one wavefront per token.
+// scales, codes (and affine zero points) are those of the per-token path
+// (same reductions, same device functions).  Any other chunk runs the
+// per-token path, one wavefront per token.
 template <int D, bool BF16, bool AFF>
 __global__ __launch_bounds__(256) void append_pages_kernel(Q8K4V_APPEND_PARAMS) {
     constexpr int EPT = D / 16;      // elements per thread (16 threads per token)
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void append_pages_kernel(Q8K4V_APPEND_PARAMS) 
     const long tok0 = (long)(blockIdx.x / H) * 16;
     if (threadIdx.x == 0) {
         int page = -1;
-        if (!AFF && tok0 + 16 <= total_new) {
+        if (tok0 + 16 <= total_new) {
             int lo = 0, hi = n_seqs - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -223,34 +223,56 @@ __global__ __launch_bounds__(256) void append_pages_kernel(Q8K4V_APPEND_PARAMS) 
     const int t = threadIdx.x, slot = t >> 4, u = t & 15;
     const size_t blk = (size_t)page * H + h;
     const size_t row = (size_t)(tok0 + slot) * H + h;
-    // keys: absmax over the token's 16 threads
+    // keys: absmax (affine: min and max) over the token's 16 threads
     float kx[EPT];
     load_seg<D, EPT, BF16>(k_new, row, u, kx);
-    float ka = 0.0f;
+    int kc[EPT];
+    _Float16 ks16;
+    int kz = 0;
+    if (AFF) {
+        float mn = kx[0], mx = kx[0];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) ka = fmaxf(ka, fabsf(kx[e]));
-    ka = wave_max(ka, 16);
-    const _Float16 ks16 = scale_of(ka, 127.0f);
-    const float ks = (float)ks16;
+        for (int e = 1; e < EPT; ++e) { mn = fminf(mn, kx[e]); mx = fmaxf(mx, kx[e]); }
+        const Affine a = affine_of(wave_min(mn, 16), wave_max(mx, 16), 255.0f);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) kc[e] = affine_code(kx[e], a, 255.0f) ^ 0x80;
+        ks16 = a.s16;
+        kz = (int)a.z ^ 0x80;
+    } else {
+        float ka = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) ka = fmaxf(ka, fabsf(kx[e]));
+        ka = wave_max(ka, 16);
+        ks16 = scale_of(ka, 127.0f);
+        const float ks = (float)ks16;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) kc[e] = code_of(kx[e], ks, 127.0f);
+    }
     uint32_t kw[EPT / 4];
 #pragma unroll
     for (int i = 0; i < EPT / 4; ++i) {
         kw[i] = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) kw[i] |= ((uint32_t)code_of(kx[4 * i + e], ks, 127.0f) & 0xFFu) << (8 * e);
+        for (int e = 0; e < 4; ++e) kw[i] |= ((uint32_t)kc[4 * i + e] & 0xFFu) << (8 * e);
     }
     int8_t* krow = k_codes + (blk * 16 + slot) * D + EPT * u;
     if constexpr (EPT == 8) *(u32x2*)krow = u32x2{kw[0], kw[1]};
     else *(uint32_t*)krow = kw[0];
-    if (u == 0) k_scales[blk * 16 + slot] = __builtin_bit_cast(uint16_t, ks16);
+    if (u == 0) {
+        k_scales[blk * 16 + slot] = __builtin_bit_cast(uint16_t, ks16);
+        if (AFF) k_zeros[blk * 16 + slot] = (int8_t)kz;
+    }
     // values: groups of 32 dimensions over TPG threads
     float vx[EPT];
     load_seg<D, EPT, BF16>(v_new, row, u, vx);
     int c[EPT];
     _Float16 vs16;
     int z;
-    value_codes<EPT, TPG, false>(vx, c, &vs16, &z);
-    if (u % TPG == 0) v_scales[(blk * 16 + slot) * NG + u / TPG] = __builtin_bit_cast(uint16_t, vs16);
+    value_codes<EPT, TPG, AFF>(vx, c, &vs16, &z);
+    if (u % TPG == 0) {
+        v_scales[(blk * 16 + slot) * NG + u / TPG] = __builtin_bit_cast(uint16_t, vs16);
+        if (AFF) v_zeros[(blk * 16 + slot) * NG + u / TPG] = (uint8_t)z;
+    }
     uint32_t nib = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) nib |= ((uint32_t)c[e] & 0xFu) << (4 * e);

@@ -32,6 +32,14 @@ def test_append_bit_exact(D, dtype):
     _assert_same(cache_to_host(upload_cache(w, codec="affine")), oracle_cache(w, codec_name="affine"))
 
 
+def test_append_bulk_prompt_bit_exact():
+    """A 4096-token prompt from position 0 in one call: every chunk of 16 new
+    tokens fills one page (the page-block path)."""
+    from tests.gpu_util import cache_to_host, upload_cache
+    w = workloads.gqa_decode_4k()
+    _assert_same(cache_to_host(upload_cache(w, codec="affine")), oracle_cache(w, codec_name="affine"))
+
+
 def test_append_edge_rows():
     """Rows that stress the rule: all zero, one-signed (lo or hi widened to
     zero), constant, exact ties, tiny (subnormal or zero scale) and huge
