@@ -133,7 +133,9 @@ Q8K4V_DEV void write_zero_rows(const AttnParams& p, const WorkItem& w, int r0, i
 // vectorised loads see them.  Thread t takes (row, float4 column) pairs and
 // a split group, loads the records of its splits in batches of CH with all
 // loads of a batch in flight, merges them online, and the split groups are
-// merged through LDS.
+// merged through LDS.  Every load of a batch is unconditional (split index
+// clamped, the extra records masked afterwards): a load under a branch gets
+// its own wait, one memory round trip per split.
 constexpr int kCombineMaxSplits = 1024;
 
 template <int D, int NR>
@@ -168,32 +170,30 @@ Q8K4V_DEV void combine_splits(const AttnParams& p, int b, int kh, int r0, int n_
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
                     const int sp = s0 + c * sg_n;
-                    if (sp < n_eff) {
-                        const float* rec = rbase + (size_t)sp * rs;
-                        m[c] = rec[0];
-                        l[c] = rec[1];
-                        o[c] = *((const f32x4*)(rec + 4) + qc);
-                    } else {
-                        m[c] = kNegInf;
-                        l[c] = 0.0f;
-                        o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    }
+                    const float* rec = rbase + (size_t)min(sp, n_eff - 1) * rs;
+                    const float2 ml = *(const float2*)rec;
+                    const f32x4 ov = *((const f32x4*)(rec + 4) + qc);
+                    const bool in = sp < n_eff;
+                    m[c] = in ? ml.x : kNegInf;
+                    l[c] = in ? ml.y : 0.0f;
+                    o[c] = in ? ov : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 }
                 float Mn = M;
 #pragma unroll
                 for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, m[c]);
-                if (Mn != kNegInf) {
-                    const float a = exp2_fast(M - Mn);
-                    O *= a;
-                    Ls *= a;
+                // branch-free (a branch here lets the compiler sink the batch's
+                // loads below it): with every maximum -inf, ref 0 gives weights 0
+                const float ref = (Mn == kNegInf) ? 0.0f : Mn;
+                const float a = exp2_fast(M - ref);        // M = -inf gives 0
+                O *= a;
+                Ls *= a;
 #pragma unroll
-                    for (int c = 0; c < CH; ++c) {
-                        const float wgt = exp2_fast(m[c] - Mn);
-                        O += o[c] * wgt;
-                        Ls += l[c] * wgt;
-                    }
-                    M = Mn;
+                for (int c = 0; c < CH; ++c) {
+                    const float wgt = exp2_fast(m[c] - ref);
+                    O += o[c] * wgt;
+                    Ls += l[c] * wgt;
                 }
+                M = Mn;
             }
             s_m[sg * chunk + pl] = M;
             s_l[sg * chunk + pl] = Ls;
@@ -343,6 +343,8 @@ Q8K4V_DEV void finish_workgroup(const AttnParams& p, const WorkItem& w, int r0,
 // kernel on the stream, so plain loads see them.  Records are loaded for
 // every split of the launch (all in bounds) and those past the sequence's
 // last split are masked afterwards, so the loads do not wait for seq_lens.
+// The split index of a batch's loads is clamped rather than branched on, so
+// the loads of a batch go out together.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     constexpr int NQ = D / 4;                 // float4 columns of a row
@@ -368,35 +370,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int s = s0 + c * SG;
-            if (s < p.n_splits) {
-                const float* rec = base + (size_t)s * rs;
-                m[c] = rec[0];
-                l[c] = rec[1];
-                o[c] = *((const f32x4*)(rec + 4) + qc);
-            }
+            const float* rec = base + (size_t)min(s, p.n_splits - 1) * rs;
+            const float2 ml = *(const float2*)rec;
+            const f32x4 ov = *((const f32x4*)(rec + 4) + qc);
+            const bool in = s < n_eff;       // selects, not a branch the loads could sink into
+            m[c] = in ? ml.x : kNegInf;
+            l[c] = in ? ml.y : 0.0f;
+            o[c] = in ? ov : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-            if (s0 + c * SG >= n_eff) {
-                m[c] = kNegInf;
-                l[c] = 0.0f;
-                o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
         float Mn = M;
 #pragma unroll
         for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, m[c]);
-        if (Mn != kNegInf) {
-            const float a = exp2_fast(M - Mn);       // M = -inf gives 0
-            O *= a;
-            Ls *= a;
+        // branch-free (a branch here lets the compiler sink the batch's
+        // loads below it): with every maximum -inf, ref 0 gives weights 0
+        const float ref = (Mn == kNegInf) ? 0.0f : Mn;
+        const float a = exp2_fast(M - ref);        // M = -inf gives 0
+        O *= a;
+        Ls *= a;
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const float wgt = exp2_fast(m[c] - Mn);
-                O += o[c] * wgt;
-                Ls += l[c] * wgt;
-            }
-            M = Mn;
+        for (int c = 0; c < CH; ++c) {
+            const float wgt = exp2_fast(m[c] - ref);
+            O += o[c] * wgt;
+            Ls += l[c] * wgt;
         }
+        M = Mn;
     }
     if (qc == 0) {
         s_m[sg] = M;
@@ -456,13 +453,12 @@ __global__ __launch_bounds__(256) void combine_cascade_kernel(const AttnParams p
         f32x4 o[CH];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int u = u0 + c * SG;
-            if (u < total) {
-                const float* rec = u < p.pre_eff ? pre + (size_t)u * pre_step : suf + (size_t)(u - p.pre_eff) * suf_step;
-                m[c] = rec[0];
-                l[c] = rec[1];
-                o[c] = *((const f32x4*)(rec + 4) + qc);
-            }
+            const int u = min(u0 + c * SG, total - 1);    // clamped: no branch around the loads
+            const float* rec = u < p.pre_eff ? pre + (size_t)u * pre_step : suf + (size_t)(u - p.pre_eff) * suf_step;
+            const float2 ml = *(const float2*)rec;
+            m[c] = ml.x;
+            l[c] = ml.y;
+            o[c] = *((const f32x4*)(rec + 4) + qc);
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
@@ -476,18 +472,19 @@ __global__ __launch_bounds__(256) void combine_cascade_kernel(const AttnParams p
         float Mn = M;
 #pragma unroll
         for (int c = 0; c < CH; ++c) Mn = fmaxf(Mn, m[c]);
-        if (Mn != kNegInf) {
-            const float a = exp2_fast(M - Mn);
-            O *= a;
-            Ls *= a;
+        // branch-free (a branch here lets the compiler sink the batch's
+        // loads below it): with every maximum -inf, ref 0 gives weights 0
+        const float ref = (Mn == kNegInf) ? 0.0f : Mn;
+        const float a = exp2_fast(M - ref);        // M = -inf gives 0
+        O *= a;
+        Ls *= a;
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const float wgt = exp2_fast(m[c] - Mn);
-                O += o[c] * wgt;
-                Ls += l[c] * wgt;
-            }
-            M = Mn;
+        for (int c = 0; c < CH; ++c) {
+            const float wgt = exp2_fast(m[c] - ref);
+            O += o[c] * wgt;
+            Ls += l[c] * wgt;
         }
+        M = Mn;
     }
     if (qc == 0) {
         s_m[sg] = M;
