@@ -357,9 +357,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     const int r = blockIdx.x % p.R;
     const int kh = (blockIdx.x / p.R) % p.H;
     const int b = blockIdx.x / (p.R * p.H);
-    const int L = p.seq_lens[b];
-    const int npages = (L + 15) >> 4;
-    const int n_eff = min(p.n_splits, (max(0, npages - p.page_lo) + p.split_pages - 1) / p.split_pages);
+    // The sequence length comes in through a vector (buffer) load and is first
+    // used after a batch's record loads are out: a scalar load of it would be
+    // waited for before them, one more memory round trip.  Buffer resource
+    // word 3 of gfx9-family targets: 32-bit data format.
+    const int L = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p.seq_lens + b), 0, 4, 0x00020000), 0, 0, 0);
     const size_t rs = (size_t)p.R * partial_stride<D>();
     const float* base = p.partials + ((size_t)b * p.H + kh) * p.n_splits * rs + (size_t)r * partial_stride<D>();
     float M = kNegInf, Ls = 0.0f;
@@ -367,16 +370,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const AttnParams p) {
     for (int s0 = sg; s0 < p.n_splits; s0 += SG * CH) {
         float m[CH], l[CH];
         f32x4 o[CH];
+        float2 ml[CH];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int s = s0 + c * SG;
-            const float* rec = base + (size_t)min(s, p.n_splits - 1) * rs;
-            const float2 ml = *(const float2*)rec;
-            const f32x4 ov = *((const f32x4*)(rec + 4) + qc);
-            const bool in = s < n_eff;       // selects, not a branch the loads could sink into
-            m[c] = in ? ml.x : kNegInf;
-            l[c] = in ? ml.y : 0.0f;
-            o[c] = in ? ov : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const float* rec = base + (size_t)min(s0 + c * SG, p.n_splits - 1) * rs;
+            ml[c] = *(const float2*)rec;
+            o[c] = *((const f32x4*)(rec + 4) + qc);
+        }
+        int Lv = L;
+        asm volatile("" : "+v"(Lv));   // keeps the length's wait below the loads
+        const int npages = (Lv + 15) >> 4;
+        const int n_eff = min(p.n_splits, (max(0, npages - p.page_lo) + p.split_pages - 1) / p.split_pages);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = s0 + c * SG < n_eff;     // selects, not a branch the loads could sink into
+            m[c] = in ? ml[c].x : kNegInf;
+            l[c] = in ? ml[c].y : 0.0f;
+            if (!in) o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         float Mn = M;
 #pragma unroll
@@ -439,8 +449,10 @@ __global__ __launch_bounds__(256) void combine_cascade_kernel(const AttnParams p
     const int g = blockIdx.x % p.R;
     const int kh = (blockIdx.x / p.R) % p.H;
     const int b = blockIdx.x / (p.R * p.H);
-    const int npages = (p.seq_lens[b] + 15) >> 4;
-    const int n_suf = min(p.n_splits, (max(0, npages - p.page_lo) + p.split_pages - 1) / p.split_pages);
+    // the sequence length as in combine_kernel: a vector load, waited for
+    // after a batch's record loads
+    const int L = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p.seq_lens + b), 0, 4, 0x00020000), 0, 0, 0);
     const float* pre = p.pre_partials + ((size_t)kh * p.pre_splits * p.pre_R + (size_t)b * p.R + g) * RS;
     const size_t pre_step = (size_t)p.pre_R * RS;
     const float* suf = p.partials + (((size_t)b * p.H + kh) * p.n_splits * p.R + g) * RS;
@@ -460,14 +472,17 @@ __global__ __launch_bounds__(256) void combine_cascade_kernel(const AttnParams p
             l[c] = ml.y;
             o[c] = *((const f32x4*)(rec + 4) + qc);
         }
+        int Lv = L;
+        asm volatile("" : "+v"(Lv));   // keeps the length's wait below the loads
+        const int npages = (Lv + 15) >> 4;
+        const int n_suf = min(p.n_splits, (max(0, npages - p.page_lo) + p.split_pages - 1) / p.split_pages);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int u = u0 + c * SG;
-            if (u >= total || (u >= p.pre_eff && u - p.pre_eff >= n_suf)) {
-                m[c] = kNegInf;
-                l[c] = 0.0f;
-                o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+            const bool in = u < total && (u < p.pre_eff || u - p.pre_eff < n_suf);   // selects
+            m[c] = in ? m[c] : kNegInf;
+            l[c] = in ? l[c] : 0.0f;
+            if (!in) o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
         float Mn = M;
 #pragma unroll
