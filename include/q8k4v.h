@@ -162,7 +162,9 @@ int32_t kv_quant_append(const q8k4v_cache *cache, const void *k_new, const void 
  * prefill.  Returns 0 on invalid shapes.  The workspace holds
  * the split-K partials and, with fused_combine, a counter area that must be
  * zero when first used; the library leaves the counters at zero after each
- * completed call, so zero the workspace once after allocating it.
+ * completed call, so zero the workspace once after allocating it.  The
+ * partials need no initial value: records of splits past a sequence's last
+ * page are masked by the merge, never read as values.
  */
 size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t max_seq_len, int32_t n_draft,
