@@ -99,23 +99,3 @@ def verify(cache: PagedCache, q: np.ndarray, q_dtype: str, page_table: np.ndarra
                     h = kvh * G + g
                     out[b, j, h] = softmax_attention(qf[b, j, h], kh[:vis], vh[:vis], c)
     return out
-
-
-def decode_rows(cache: PagedCache, q: np.ndarray, q_dtype: str, page_table: np.ndarray,
-                seq_lens: np.ndarray, softmax_scale: float, rows) -> np.ndarray:
-    """Decode output for selected (b, h) pairs only -- used to sample full-size
-    outputs one by one.  Returns fp64 ``[len(rows)][D]``."""
-    qf = as_f32(q, q_dtype).astype(np.float64)
-    Hq = qf.shape[1]
-    G = Hq // cache.num_kv_heads
-    c = _scale64(softmax_scale)
-    res = []
-    cached = {}
-    for b, h in rows:
-        key = (b, h // G)
-        if key not in cached:
-            cached.clear()
-            cached[key] = sequence_kv(cache, page_table[b], int(seq_lens[b]), h // G)
-        kh, vh = cached[key]
-        res.append(softmax_attention(qf[b, h], kh, vh, c))
-    return np.stack(res)
