@@ -4,17 +4,23 @@ One step = one decode step of one layer at 64K context: quantize-and-append
 the new token's key/value (32 query / 8 kv heads, D 128, bf16) and attend the
 65536 cached tokens with the single bf16 query token.  Steps rotate over
 distinct layer caches whose total size exceeds 4 x 256 MiB (the MI355X
-last-level cache), so every step streams its cache from HBM.
+last-level cache), so every step streams its cache from HBM.  After W eager
+warm-up steps, exactly K steps are captured in one HIP graph; one untimed
+replay is checked against the eager result, and one replay is timed with
+HIP events on the stream it runs on.
 
 Prints one JSON line.  ``value`` is the achieved algorithmic HBM bandwidth of
 the whole step (GB/s); ``tok_s_per_layer`` is query tokens per second per
-layer; ``roofline`` reports the attention kernel alone, timed with HIP events
-on the stream it runs on.  ``cpu_baseline`` times the CPU oracle on the same
-workload (a bounded number of steps).  ``--cpu-report`` only times the CPU
-oracle on every workload, at the default BLAS pool and at one thread.
+layer; ``roofline`` reports the attention launch alone (a K-launch graph of
+it, timed the same way); ``probe`` streams the same page-head blocks with no
+compute (q8k4v_hbm_probe) and a contiguous buffer (q8k4v_stream_probe):
+what the memory system gives this access pattern, the attention launch's
+practical ceiling; ``cpu_baseline`` times the CPU oracle on the same
+workload (a bounded number of steps).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-    python bench.py --cpu-report
+    python bench.py [--steps K] [--warmup W] [--workload NAME|all] [--no-cpu-baseline]
+    python bench.py --cpu-report       # the oracle on every workload, default BLAS pool and one thread
+    python bench.py --tune             # tune_select first, gated by the stored oracle references
 """
 
 from __future__ import annotations
@@ -32,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
+WORKLOADS = ["tiny_decode_256", "gqa_decode_4096", "gqa_decode_65536", "verify_65536_w8", "multi_session_16x32768"]
+TUNE_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q8kv_d128_w8.npz")
 
 
 def cache_bytes_per_token_head(D: int, affine: bool = False) -> int:
@@ -45,12 +53,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa_decode_65536",
-                    choices=["gqa_decode_65536", "gqa_decode_4096", "verify_65536_w8", "multi_session_16x32768"])
+    ap.add_argument("--workload", default="gqa_decode_65536", choices=WORKLOADS + ["all"],
+                    help="all: one JSON line per workload (attention launches, no CPU baseline)")
     ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0: enough for 4x LLC)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=20)
-    ap.add_argument("--tune", action="store_true", help="run tune_select first and use its choice")
+    ap.add_argument("--tune", action="store_true",
+                    help="run tune_select first (oracle gate from the stored references) and use its choice")
+    ap.add_argument("--tune-budget-ms", type=int, default=60000)
+    ap.add_argument("--tune-report", default="", help="write tune_select's JSON report to this file")
     ap.add_argument("--config", default="", help="JSON dict of launch config fields")
     ap.add_argument("--kernel-only", action="store_true", help="time only the attention launches (profiling)")
     ap.add_argument("--contiguous-pages", action="store_true", help="identity page table (profiling)")
@@ -70,7 +82,9 @@ def parse():
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU (--gpus must be 1): across GPUs the path "
+                                   "would shard by kv head or by session, with no communication, and no "
+                                   "multi-GPU figure is measured"}))
         return 2
     if args.cpu_report:
         return cpu_report()
@@ -85,7 +99,67 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    w = workloads.NAMED[args.workload]()
+    cfg = q8.make_config(**json.loads(args.config)) if args.config else None
+    tuned = None
+    if args.tune:
+        dcfg, vcfg, rep = run_tuner(torch, q8, workloads, args.tune_budget_ms)
+        if args.tune_report:
+            with open(args.tune_report, "w") as f:
+                json.dump(rep, f)
+        w0 = workloads.NAMED[args.workload if args.workload != "all" else "gqa_decode_65536"]()
+        cfg = vcfg if w0.n_draft else dcfg
+        tuned = {"decode": dcfg.as_dict(), "verify": vcfg.as_dict(),
+                 "status": rep.get("status"), "units": [{k: u.get(k) for k in
+                                                          ("unit", "qualified", "chosen_cost", "oracle_gate",
+                                                           "admitted", "rejected", "rejected_by", "invalid")}
+                                                         for u in rep.get("units", [])]}
+
+    names = WORKLOADS if args.workload == "all" else [args.workload]
+    for name in names:
+        w = workloads.NAMED[name]()
+        res = run_workload(args, torch, q8, w, cfg, tuned, full_line=args.workload != "all")
+        if args.workload != "all" and not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline(w, args.cpu_steps, res["step_bytes"], res["tokens_per_step"])
+        print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_tuner(torch, q8, workloads, budget_ms):
+    """tune_select over decode / verify at 4096 and 65536 tokens (32 q / 8 kv
+    heads, D 128, 8 drafts), each term gated by the oracle outputs stored in
+    tests/golden (written by tests/golden/make_tune_refs.py) at 2e-3 sigma."""
+    z = np.load(TUNE_REFS)
+    refs = {}
+    keep = []
+    for size, ctx, seed in (("small", 4096, 11), ("large", 65536, 12)):
+        w = workloads.tune_reference(ctx, 8, seed)
+        cache = q8.PagedKVCache(w.num_pages, w.num_kv_heads, w.head_dim)
+        for a in w.appends:
+            q8.kv_quant_append(cache, _dev(torch, a.k, True), _dev(torch, a.v, True), _dev(torch, a.cu_new),
+                               _dev(torch, a.start_pos), _dev(torch, a.page_table))
+        pt = _dev(torch, np.ascontiguousarray(w.page_table[0]))
+        keep.append(cache)
+        sigma = z["sigma_" + size]
+        refs["decode_" + size] = {"cache": cache, "q": _dev(torch, np.ascontiguousarray(w.q[0, 0]), True),
+                                  "page_table": pt, "length": ctx, "out": z["decode_" + size], "sigma": sigma}
+        refs["verify_" + size] = {"cache": cache, "q": _dev(torch, np.ascontiguousarray(w.q[0]), True),
+                                  "page_table": pt, "length": ctx + 8, "out": z["verify_" + size], "sigma": sigma}
+    torch.cuda.synchronize()
+    return q8.tune_select(32, 8, 128, n_draft=8, ctx_small=4096, ctx_large=65536, budget_ms=budget_ms,
+                          install=True, refs=refs, ref_tol=2e-3)
+
+
+def _dev(torch, a, bf=False):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if bf:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.to("cuda:0")
+
+
+def run_workload(args, torch, q8, w, cfg, tuned, full_line: bool) -> dict:
+    """Times exactly args.steps steps of workload w (and as many attention
+    launches, and the probes) and returns the JSON record."""
+    dev = torch.device("cuda:0")
     if args.contiguous_pages:
         # relabel physical pages so that sequence 0's pages are in logical order
         perm = np.argsort(w.page_table[0][: (int(w.seq_lens[0]) + 15) // 16])
@@ -100,14 +174,10 @@ def main() -> int:
     unique = w.unique_tokens()
     layer_bytes = w.num_pages * H * 16 * per_th
     layers = args.layers or max(2, -(-4 * LLC_BYTES // layer_bytes) + 1)
-
-    def to_dev(a, bf=False):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        if bf:
-            t = t.view(torch.int16).view(torch.bfloat16)
-        return t.to(dev)
+    K = args.steps
 
     bf = w.dtype == "bf16"
+    to_dev = lambda a, b=False: _dev(torch, a, b)
     caches = [q8.PagedKVCache(w.num_pages, H, D, codec=args.codec) for _ in range(layers)]
     batches = [(to_dev(a.k, bf), to_dev(a.v, bf), to_dev(a.cu_new), to_dev(a.start_pos), to_dev(a.page_table))
                for a in w.appends]
@@ -115,6 +185,7 @@ def main() -> int:
         for (k, v, cu, sp, pt) in batches:
             q8.kv_quant_append(c, k, v, cu, sp, pt)
     torch.cuda.synchronize()
+    del batches
     # the step's new token: the last cached token of every sequence, re-appended
     last = w.appends[-1]
     B = w.n_seqs
@@ -127,12 +198,6 @@ def main() -> int:
     seq_lens = to_dev(w.seq_lens)
     q = to_dev(w.q, bf)
     msl = int(w.seq_lens.max())
-    cfg = q8.make_config(**json.loads(args.config)) if args.config else None
-    tuned = None
-    if args.tune:
-        dcfg, vcfg, rep = q8.tune_select(Hq, H, D, n_draft=max(1, w.n_draft or 8), install=True)
-        cfg = vcfg if w.n_draft else dcfg
-        tuned = cfg.as_dict()
     nd = w.n_draft
     # sessions over one shared prefix run the prefix cascade
     n_pref = 0 if (nd or args.no_cascade) else w.shared_prefix // 16
@@ -166,59 +231,59 @@ def main() -> int:
         q8.kv_quant_append(c, step_k, step_v, step_cu, step_pos, page_table, total_new=B)
         attend(c)
 
-    # Steps are captured in HIP graphs (one graph = one pass over all layer
-    # caches) so that the timing sees device work, not host launch overhead.
-    def capture(fn):
+    # a graph of exactly n calls of fn(i), i = 0 .. n-1 (rotating layers)
+    def capture(fn, n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(layers):
+            for i in range(n):
                 fn(i)
         return g
 
-    def timed(g, reps):
+    def timed(g, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(reps):
-            g.replay()
+        g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * layers)
+        return e0.elapsed_time(e1) / n
 
-    # eager reference of the last layer, then every graph replay must match it
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    attend(caches[layers - 1])
+    # eager reference of the last step's layer; the graphs' untimed replay must match it
+    last_layer = (K - 1) % layers
+    attend(caches[last_layer])
     torch.cuda.synchronize()
     ref_out = out.clone()
-    step_graph = capture(step)
-    attn_graph = capture(lambda i: attend(caches[i]))
-    reps = max(1, -(-args.steps // layers))
+    step_graph = capture(step, K)
+    attn_graph = capture(lambda i: attend(caches[i % layers]), K)
     for g in (step_graph, attn_graph):
-        for _ in range(3):
-            out.zero_()
-            g.replay()
-            torch.cuda.synchronize()
-            if not torch.equal(out, ref_out):
-                raise RuntimeError("graph replay differs from the eager result")
-            attend(caches[layers - 1])          # eager work between replays
-            torch.cuda.synchronize()
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref_out):
+            raise RuntimeError("graph replay differs from the eager result")
     t0 = time.perf_counter()
-    ms_step = timed(attn_graph if args.kernel_only else step_graph, reps)
+    ms_step = timed(attn_graph if args.kernel_only else step_graph, K)
     wall = time.perf_counter() - t0
-    ms_attn = timed(attn_graph, reps)
-    args.steps = reps * layers
+    ms_attn = timed(attn_graph, K)
+    del step_graph, attn_graph
 
     q_bytes = q.numel() * q.element_size()
     o_bytes = out.numel() * 4
-    attn_bytes = unique * H * per_th + q_bytes + o_bytes
+    cache_read = unique * H * per_th
+    attn_bytes = cache_read + q_bytes + o_bytes
     elem = 2 if bf else 4
     append_bytes = B * H * D * 2 * elem + B * H * per_th
     step_bytes = attn_bytes + (0 if args.kernel_only else append_bytes)
     tokens = B * max(1, nd)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = attn_bytes / (ms_attn * 1e-3) / 1e9
+
+    probe = None
+    if not args.no_probe and args.codec == "symmetric":
+        probe = run_probes(torch, q8, caches, seq_lens, msl, page_table, K, layers, cache_read, w, n_pref)
 
     res = {
         "metric": "achieved HBM GB/s (% of peak) + decode tok/s/layer, q8K/q4V attn at 64K ctx",
@@ -227,13 +292,13 @@ def main() -> int:
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tok_s_per_layer": round(tokens / (ms_step * 1e-3), 1),
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, int8 K / int4 V codes, fp16 MACs, fp32 accumulate",
+        "dtype": "bf16 in, int8 K / int4 V codes, int8 and fp16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded N(0,1), 1% outlier channels x8, bf16), random page permutation",
         "config": {"workload": w.name, "codec": args.codec, "num_q_heads": Hq, "num_kv_heads": H, "head_dim": D,
                    "context": int(w.seq_lens.max()), "n_seqs": B, "n_draft": nd, "page_size": 16,
@@ -241,20 +306,72 @@ def main() -> int:
                    "launch_config": tuned or (cfg.as_dict() if cfg else "default"),
                    "shared_prefix_pages": n_pref},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(w.name if args.codec == "symmetric" else w.name + "_affine", nd),
-                     "kernel": ("attn_decode_prefix_q8k4v launch (prefix-pass kernel + suffix-pass kernel"
-                                " + LSE combine kernel)" if n_pref else
-                                ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v")
-                                + " launch (split-K attention kernel + LSE combine kernel)"),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_bytes(w.name if args.codec == "symmetric" else w.name + "_affine", nd),
+                     "kernel": attention_launch_name(nd, n_pref, w, cfg, q8),
                      "algorithmic_bytes": attn_bytes, "avg_launch_us": round(ms_attn * 1e3, 3)},
+        "tokens_per_step": tokens,
         "step_bytes": step_bytes,
         "wall_s": round(wall, 3),
-        "device": device_info(torch),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_steps, step_bytes, tokens)
-    print(json.dumps(res), flush=True)
-    return 0
+    if probe:
+        res["probe"] = probe
+        res["pct_of_probe"] = round(100 * achieved / probe["paged_GBs"], 1)
+    if full_line:
+        res["device"] = device_info(torch)
+    return res
+
+
+def attention_launch_name(nd, n_pref, w, cfg, q8) -> str:
+    if n_pref:
+        return "attn_decode_prefix_q8k4v launch (prefix and suffix passes + cascade combine kernel)"
+    fused = bool(cfg and cfg.fused_combine)
+    return ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v") + (
+        " launch (split-K attention kernel with the in-launch split merge)" if fused else
+        " launch (split-K attention kernel + LSE combine kernel)")
+
+
+def run_probes(torch, q8, caches, seq_lens, msl, page_table, K, layers, cache_read, w, n_pref):
+    """The streaming references: q8k4v_hbm_probe over the same caches
+    (rotating as the steps do; the best of its launch shapes) and
+    q8k4v_stream_probe over contiguous 256 MiB slices of a 2 GiB buffer."""
+    stream = torch.cuda.current_stream()
+
+    def time_graph(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    res = {"paged_bytes": cache_read}
+    if not n_pref:   # the probe streams each sequence's own pages (a shared prefix would be re-read)
+        best = None
+        for waves, stages in ((4, 2), (4, 3), (4, 4), (8, 2), (8, 3)):
+            ms = time_graph(lambda i: q8.hbm_probe(caches[i % layers], seq_lens, msl, page_table, waves, stages),
+                            min(K, 4 * layers))
+            gbs = cache_read / (ms * 1e-3) / 1e9
+            res[f"paged_GBs_w{waves}s{stages}"] = round(gbs, 1)
+            if best is None or gbs > best[0]:
+                best = (gbs, ms, waves, stages)
+        res["paged_GBs"] = round(best[0], 1)
+        res["paged_us"] = round(best[1] * 1e3, 3)
+        res["paged_shape"] = {"waves_per_wg": best[2], "stages": best[3]}
+    seg = 256 << 20
+    buf = torch.empty(8 * seg, dtype=torch.uint8, device="cuda:0")
+    ms = time_graph(lambda i: q8.stream_probe(buf[(i % 8) * seg:(i % 8 + 1) * seg], 8, 3), 16)
+    res["stream_GBs"] = round(seg / (ms * 1e-3) / 1e9, 1)
+    del buf
+    if "paged_GBs" not in res:
+        res["paged_GBs"] = res["stream_GBs"]
+    return res
 
 
 # Kernel sources whose HBM traffic the committed counter summary describes;

@@ -55,15 +55,23 @@ class Config(C.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class TuneRef(C.Structure):
+    _fields_ = [("cache", C.POINTER(CacheDesc)), ("q", C.c_void_p), ("page_table", C.c_void_p),
+                ("len", C.c_int32), ("max_pages", C.c_int32), ("out", C.c_void_p), ("sigma", C.c_void_p)]
+
+
 class TuneRequest(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("n_draft", C.c_int32), ("ctx_small", C.c_int32), ("ctx_large", C.c_int32),
                 ("budget_ms", C.c_int64), ("mem_cap_bytes", C.c_size_t), ("seed", C.c_uint64),
                 ("install", C.c_int32), ("max_candidates", C.c_int32),
-                ("ref_cache", C.POINTER(CacheDesc)), ("ref_q", C.c_void_p), ("ref_q_verify", C.c_void_p),
-                ("ref_page_table", C.c_void_p), ("ref_len", C.c_int32), ("ref_max_pages", C.c_int32),
-                ("ref_out", C.c_void_p), ("ref_out_verify", C.c_void_p), ("ref_tol", C.c_float),
+                ("ref", TuneRef * 4), ("ref_tol", C.c_float),
                 ("softmax_scale", C.c_float), ("record_path", C.c_char_p)]
+
+
+# the four terms of the tuner's service cost, in the order of
+# q8k4v_tune_request.ref
+TUNE_TERMS = ("decode_small", "decode_large", "verify_small", "verify_large")
 
 
 _lib = None
@@ -110,6 +118,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
                                       C.c_float, C.POINTER(Config), vp, sz, vp]
     lib.tune_select.restype = i32
     lib.tune_select.argtypes = [C.POINTER(TuneRequest), C.POINTER(Config), C.c_char_p, sz]
+    lib.q8k4v_hbm_probe.restype = i32
+    lib.q8k4v_hbm_probe.argtypes = [C.POINTER(CacheDesc), i32, vp, i32, vp, i32, i32, i32, vp]
+    lib.q8k4v_stream_probe.restype = i32
+    lib.q8k4v_stream_probe.argtypes = [vp, sz, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -363,33 +375,42 @@ def attn_verify_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_t
 def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int = 8,
                 ctx_small: int = 4096, ctx_large: int = 65536, budget_ms: int = 60000,
                 mem_cap_bytes: int = 0, seed: int = 0, install: bool = False, max_candidates: int = 0,
-                ref=None, report_cap: int = 1 << 20, record_path: Optional[str] = None):
-    """Runs the on-device tuner.  ``ref`` (optional) is a dict with keys
-    ``cache`` (PagedKVCache), ``q``, ``q_verify``, ``page_table`` (device),
-    ``length``, ``out``, ``out_verify`` (host float32 numpy) and ``tol``.
-    ``record_path`` (optional): file of stored choices, reused for the same
-    device identity and request shape.  Returns (decode Config, verify
-    Config, report dict)."""
+                refs=None, ref_tol: float = 0.0, report_cap: int = 1 << 20,
+                record_path: Optional[str] = None):
+    """Runs the on-device tuner.  ``refs`` (optional): a dict keyed by
+    :data:`TUNE_TERMS` (``decode_small``, ``decode_large``, ``verify_small``,
+    ``verify_large``), each a dict with ``cache`` (PagedKVCache), ``q``
+    (device bf16 ``[n][Hq][D]``), ``page_table`` (device int32, one
+    sequence's pages), ``length``, ``out`` (host float32 ``[n][Hq][D]``,
+    the expected output) and optionally ``sigma`` (host ``[Hq][D]``, which
+    normalises the deviation); ``ref_tol`` bounds it.  ``record_path`` (optional): file of
+    stored choices, reused for the same device identity and request shape.
+    Returns (decode Config, verify Config, report dict)."""
+    import numpy as np
     lib = load_library()
     req = TuneRequest()
     req.num_q_heads, req.num_kv_heads, req.head_dim, req.n_draft = num_q_heads, num_kv_heads, head_dim, n_draft
     req.ctx_small, req.ctx_large, req.budget_ms = ctx_small, ctx_large, budget_ms
     req.mem_cap_bytes, req.seed, req.install, req.max_candidates = mem_cap_bytes, seed, int(install), max_candidates
     keep = []
-    if ref is not None:
-        import numpy as np
-        out = np.ascontiguousarray(ref["out"], dtype=np.float32)
-        outv = np.ascontiguousarray(ref["out_verify"], dtype=np.float32)
-        keep += [out, outv]
-        req.ref_cache = C.pointer(ref["cache"].desc)
-        req.ref_q = ref["q"].data_ptr()
-        req.ref_q_verify = ref["q_verify"].data_ptr()
-        req.ref_page_table = ref["page_table"].data_ptr()
-        req.ref_len = int(ref["length"])
-        req.ref_max_pages = int(ref["page_table"].numel())
-        req.ref_out = out.ctypes.data
-        req.ref_out_verify = outv.ctypes.data
-        req.ref_tol = float(ref["tol"])
+    for k, term in enumerate(TUNE_TERMS):
+        r = (refs or {}).get(term)
+        if r is None:
+            continue
+        out = np.ascontiguousarray(r["out"], dtype=np.float32)
+        keep.append(out)
+        pt = r["page_table"]
+        req.ref[k].cache = C.pointer(r["cache"].desc)
+        req.ref[k].q = _ptr(r["q"], "q").value
+        req.ref[k].page_table = _ptr(pt, "page_table", i32=True).value
+        req.ref[k].len = int(r["length"])
+        req.ref[k].max_pages = int(pt.numel())
+        req.ref[k].out = out.ctypes.data
+        if r.get("sigma") is not None:
+            sig = np.ascontiguousarray(r["sigma"], dtype=np.float32)
+            keep.append(sig)
+            req.ref[k].sigma = sig.ctypes.data
+    req.ref_tol = float(ref_tol)
     if record_path is not None:
         req.record_path = os.fsencode(record_path)
     table = (Config * 2)()
@@ -404,7 +425,29 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
     return table[0], table[1], report
 
 
+def hbm_probe(cache: PagedKVCache, seq_lens, max_seq_len: int, page_table, waves_per_wg: int = 4,
+              stages: int = 3, stream=None) -> None:
+    """Streams the page-head blocks a decode launch over ``cache`` reads
+    (same split and mapping, HBM -> LDS, no compute): the memory system's
+    rate for that access pattern."""
+    lib = load_library()
+    rc = lib.q8k4v_hbm_probe(C.byref(cache.desc), int(seq_lens.shape[0]), _ptr(seq_lens, "seq_lens", i32=True),
+                             int(max_seq_len), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
+                             int(waves_per_wg), int(stages), _stream(stream))
+    _check("q8k4v_hbm_probe", rc)
+
+
+def stream_probe(buf, waves_per_wg: int = 4, stages: int = 3, stream=None) -> None:
+    """Streams the bytes of the contiguous device tensor ``buf`` into LDS
+    (the sequential reference rate)."""
+    lib = load_library()
+    rc = lib.q8k4v_stream_probe(_ptr(buf, "buf"), buf.numel() * buf.element_size(), int(waves_per_wg), int(stages),
+                                _stream(stream))
+    _check("q8k4v_stream_probe", rc)
+
+
 __all__ = ["kv_quant_append", "attn_decode_q8k4v", "attn_decode_prefix_q8k4v", "attn_verify_q8k4v",
-           "attn_prefill_q8k4v", "attn_decode_append_q8k4v", "tune_select",
+           "attn_prefill_q8k4v", "attn_decode_append_q8k4v", "tune_select", "hbm_probe", "stream_probe",
+           "TUNE_TERMS",
            "workspace_bytes", "prefix_workspace_bytes",
            "PagedKVCache", "Config", "make_config", "load_library", "version", "Q8K4VError", "LIB_PATH"]

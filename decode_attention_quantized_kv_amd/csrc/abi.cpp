@@ -18,9 +18,6 @@
 
 namespace q8k4v {
 
-int32_t launch_valu(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
-int32_t launch_bmfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
-int32_t launch_mfma(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_dec2(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_rows(const AttnParams& kp, const Plan& plan, int head_dim, bool qbf16, hipStream_t stream);
 int32_t launch_combine(const AttnParams& kp, int head_dim, int rows_per_wg, hipStream_t stream);
@@ -85,13 +82,10 @@ bool dec2_rows(int32_t rows) { return rows == 1 || rows == 2 || rows == 4 || row
 // launch shape defaults per kernel; the row-block kernel takes 8 waves once
 // two row blocks share the page stream (more than 16 rows per kv head)
 void kernel_defaults(int32_t kernel, int32_t rows, q8k4v_config* c) {
-    switch (kernel) {
-        case kDec2: c->wgs_per_cu = 1; c->waves_per_wg = 4; c->stages = 2; c->tile_pages = 2; break;
-        case kRows: c->wgs_per_cu = 1; c->waves_per_wg = rows > 16 ? 8 : 4; c->stages = 2; c->tile_pages = 2; break;
-        case kMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 2; break;
-        case kBlockMfma: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
-        default: c->wgs_per_cu = 5; c->waves_per_wg = 2; c->stages = 0; c->tile_pages = 4; break;
-    }
+    c->wgs_per_cu = 1;
+    c->stages = 2;
+    c->tile_pages = 2;
+    c->waves_per_wg = (kernel == kRows && rows > 16) ? 8 : 4;
 }
 
 int32_t auto_kernel(int32_t rows) { return dec2_rows(rows) ? kDec2 : kRows; }
@@ -160,22 +154,12 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     int32_t kernel;
     switch (cfg.variant) {
         case 0: kernel = auto_kernel(rows); break;
-        case 1:
-            if (rows != 1 && rows != 2 && rows != 4 && rows != 8)
-                return fail(Q8K4V_EINVAL, "attention: variant 1 needs 1, 2, 4 or 8 rows per kv head");
-            kernel = kVector;
-            break;
-        case 2:
-            if (rows != 4 && rows != 8) return fail(Q8K4V_EINVAL, "attention: variant 2 needs 4 or 8 rows per kv head");
-            kernel = kBlockMfma;
-            break;
-        case 3: kernel = kMfma; break;
         case 4:
             if (!dec2_rows(rows)) return fail(Q8K4V_EINVAL, "attention: variant 4 needs 1, 2, 4, 8 or 16 rows per kv head");
             kernel = kDec2;
             break;
         case 5: kernel = kRows; break;
-        default: return fail(Q8K4V_EINVAL, "attention: variant must be 0..5");
+        default: return fail(Q8K4V_EINVAL, "attention: variant must be 0 (automatic), 4 or 5");
     }
     q8k4v_config kd;
     std::memset(&kd, 0, sizeof(kd));
@@ -183,34 +167,19 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     if (cfg.wgs_per_cu <= 0) cfg.wgs_per_cu = kd.wgs_per_cu;
     if (cfg.stages <= 0) cfg.stages = kd.stages;
     if (cfg.waves_per_wg <= 0) cfg.waves_per_wg = kd.waves_per_wg;
-    if (a.cache->codec == Q8K4V_CODEC_AFFINE && kernel != kDec2 && kernel != kRows)
-        return fail(Q8K4V_EUNSUPPORTED, "attention: an affine cache runs on variants 4 and 5 only");
-    if (kernel == kDec2) {
-        if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
-            return fail(Q8K4V_EINVAL, "attention: variant 4 needs 2, 4 or 8 waves per workgroup");
-    } else if (kernel == kRows) {
-        if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
-            return fail(Q8K4V_EINVAL, "attention: variant 5 needs 2, 4 or 8 waves per workgroup");
-    } else if (cfg.waves_per_wg != 1 && cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4) {
-        return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 1, 2 or 4");
-    }
-    if ((kernel == kDec2 || kernel == kRows) && cfg.stages != 2 && cfg.stages != 3)
-        return fail(Q8K4V_EINVAL, "attention: stages must be 2 or 3");
-    // tiles: the MFMA kernels fix their tile length
-    if (kernel == kBlockMfma) cfg.tile_pages = 4;
-    else if (kernel == kMfma || kernel == kDec2 || kernel == kRows) cfg.tile_pages = 2;
-    else if (cfg.tile_pages <= 0) cfg.tile_pages = kd.tile_pages;
-    if (cfg.tile_pages != 1 && cfg.tile_pages != 2 && cfg.tile_pages != 4)
-        return fail(Q8K4V_EINVAL, "attention: tile_pages must be 1, 2 or 4");
-    const bool dense = kernel == kMfma || kernel == kRows;
+    if (cfg.waves_per_wg != 2 && cfg.waves_per_wg != 4 && cfg.waves_per_wg != 8)
+        return fail(Q8K4V_EINVAL, "attention: waves_per_wg must be 2, 4 or 8");
+    if (cfg.stages != 2 && cfg.stages != 3) return fail(Q8K4V_EINVAL, "attention: stages must be 2 or 3");
+    if (cfg.tile_pages != 0 && cfg.tile_pages != 2)
+        return fail(Q8K4V_EINVAL, "attention: tile_pages must be 0 or 2 (both kernels stage 2-page tiles)");
+    cfg.tile_pages = 2;
 
     plan->rows = rows;
     plan->kernel = kernel;
-    plan->mfma = dense;
     plan->tile_pages = cfg.tile_pages;
     plan->waves = cfg.waves_per_wg;
     plan->stages = cfg.stages;
-    plan->rows_per_wg = (kernel == kMfma || kernel == kRows) ? (rows > 16 ? 32 : 16) : rows;
+    plan->rows_per_wg = kernel == kRows ? (rows > 16 ? 32 : 16) : rows;
     plan->row_chunks = (rows + plan->rows_per_wg - 1) / plan->rows_per_wg;
     const int32_t max_np = std::max(1, (a.max_seq_len + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE);
     const int32_t unit = cfg.tile_pages * cfg.waves_per_wg;      // pages per workgroup step
@@ -224,7 +193,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         sp = round_up((int32_t)((max_np + splits - 1) / splits), unit);
     }
     sp = std::max(sp, unit);
-    if ((kernel == kDec2 || kernel == kRows) && sp > 64 * cfg.waves_per_wg) {
+    if (sp > 64 * cfg.waves_per_wg) {
         // a wave's page ids sit one per lane: at most 64 pages per wave.  With
         // the automatic split of a one-chunk query block (decode, small
         // verify), the extra splits this forces are made even: a multiple of
@@ -253,22 +222,29 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
         plan->split_pages = sp;
         plan->n_splits = (max_np + sp - 1) / sp;
     }
-    if ((kernel == kDec2 || kernel == kRows) && plan->split_pages > 64 * cfg.waves_per_wg)
-        return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long for variants 4 and 5 (more than 1024 splits)");
+    if (plan->split_pages > 64 * cfg.waves_per_wg)
+        return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long (more than 1024 splits of 64 pages per wave)");
     // a multiple of 8 splits lets the kernels deal each sequence's splits
     // round robin over the 8 XCDs (the extra splits hold no pages)
     if (plan->n_splits > 1) plan->n_splits = round_up(plan->n_splits, 8);
-    plan->fused_combine = (plan->n_splits > 1 && cfg.fused_combine) ? 1 : 0;
+    // the in-launch merge keeps one arrival counter per (sequence, kv head,
+    // row chunk) in the workspace header; a launch with more items than the
+    // header holds merges with the separate combine kernel instead
+    const int64_t n_ctr = (int64_t)a.n_seqs * H * plan->row_chunks;
+    plan->fused_combine = (plan->n_splits > 1 && cfg.fused_combine && n_ctr <= kMaxCounters) ? 1 : 0;
     const size_t rec = (size_t)(a.cache->head_dim + 4) * sizeof(float);
     plan->partial_bytes = plan->n_splits > 1 ? (size_t)a.n_seqs * H * plan->n_splits * rows * rec : 0;
     plan->partial_bytes = (plan->partial_bytes + 255) / 256 * 256;
-    plan->counter_bytes = plan->fused_combine ? (size_t)a.n_seqs * H * plan->row_chunks * sizeof(uint32_t) : 0;
+    plan->counter_bytes = plan->fused_combine ? (size_t)n_ctr * sizeof(uint32_t) : 0;
     if ((int64_t)a.n_seqs * H * plan->n_splits * plan->row_chunks + 8 > 0x7FFFFFFFLL)
         return fail(Q8K4V_EINVAL, "attention: launch too large");
     return Q8K4V_OK;
 }
 
-size_t plan_workspace(const Plan& p) { return p.partial_bytes + p.counter_bytes; }
+// Every plan that writes split records puts them behind the header, fused
+// or not, so the header's counters are never overwritten by another plan's
+// records; a single-split plan writes nothing to the workspace.
+size_t plan_workspace(const Plan& p) { return p.partial_bytes ? Q8K4V_WS_HEADER_BYTES + p.partial_bytes : 0; }
 
 namespace {
 // Kernel parameters of one plain launch (no page offsets, no cascade).
@@ -281,8 +257,8 @@ AttnParams launch_params(const AttnArgs& a, const Plan& plan, void* workspace) {
     kp.v_scales = c.v_scales;
     kp.q = a.q;
     kp.out = a.out;
-    kp.partials = (float*)workspace;
-    kp.counters = plan.counter_bytes ? (uint32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
+    kp.partials = plan.partial_bytes ? (float*)((char*)workspace + Q8K4V_WS_HEADER_BYTES) : nullptr;
+    kp.counters = plan.counter_bytes ? (uint32_t*)workspace : nullptr;
     kp.seq_lens = a.seq_lens;
     kp.page_table = a.page_table;
     kp.H = c.num_kv_heads;
@@ -305,13 +281,7 @@ AttnParams launch_params(const AttnArgs& a, const Plan& plan, void* workspace) {
 }
 
 int32_t launch_kernel(const AttnParams& kp, const Plan& plan, int head_dim, bool bf, hipStream_t stream) {
-    switch (plan.kernel) {
-        case kVector: return launch_valu(kp, plan, head_dim, bf, stream);
-        case kBlockMfma: return launch_bmfma(kp, plan, head_dim, bf, stream);
-        case kDec2: return launch_dec2(kp, plan, head_dim, bf, stream);
-        case kRows: return launch_rows(kp, plan, head_dim, bf, stream);
-        default: return launch_mfma(kp, plan, head_dim, bf, stream);
-    }
+    return plan.kernel == kDec2 ? launch_dec2(kp, plan, head_dim, bf, stream) : launch_rows(kp, plan, head_dim, bf, stream);
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -366,7 +336,6 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     pp = Plan{};
     pp.rows = (int32_t)rows;
     pp.kernel = kRows;
-    pp.mfma = 1;
     pp.tile_pages = 2;
     // 8 waves for a large prefix block on its own; 4 when it shares the
     // launch with a four-wave, two-stage replicated-row suffix pass
@@ -394,15 +363,21 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     return Q8K4V_OK;
 }
 
+// The cascade's records sit behind the workspace header too (it keeps no
+// counters), so one workspace serves every entry point.
+size_t cascade_workspace(const CascadePlan& cp) {
+    return Q8K4V_WS_HEADER_BYTES + cp.pre.partial_bytes + cp.suf.partial_bytes;
+}
+
 int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-    const size_t need = cp.pre.partial_bytes + cp.suf.partial_bytes;
+    const size_t need = cascade_workspace(cp);
     if (!workspace || workspace_bytes < need)
         return fail(Q8K4V_EWORKSPACE, "attention: workspace needs " + std::to_string(need) + " bytes");
     const int D = a.cache->head_dim;
     const bool bf = a.q_dtype == Q8K4V_BF16;
-    float* pre_part = (float*)workspace;
-    float* suf_part = (float*)((char*)workspace + cp.pre.partial_bytes);
+    float* pre_part = (float*)((char*)workspace + Q8K4V_WS_HEADER_BYTES);
+    float* suf_part = (float*)((char*)workspace + Q8K4V_WS_HEADER_BYTES + cp.pre.partial_bytes);
 
     AttnParams pre = launch_params(a, cp.pre, pre_part);
     pre.partials = pre_part;
@@ -533,7 +508,7 @@ size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t
         fake.v_zeros = (uint8_t*)1;
         CascadePlan cp;
         if (make_plan(a, cfg, &cp.suf) == Q8K4V_OK && make_cascade_plan(a, n_prefix_pages, cfg, &cp) == Q8K4V_OK)
-            need = std::max(need, cp.pre.partial_bytes + cp.suf.partial_bytes);
+            need = std::max(need, cascade_workspace(cp));
     }
     g_last_error = saved;
     return need;

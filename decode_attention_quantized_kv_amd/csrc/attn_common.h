@@ -51,17 +51,6 @@ struct AttnParams {
 
 constexpr float kNegInf = -__builtin_inff();
 
-// Split partials cross XCDs (each XCD has its own L2).  They are written with
-// agent-scope atomic stores, which write through to the device-coherent level,
-// and read back with agent-scope atomic loads, so the merge needs no L2
-// writeback or invalidation.
-Q8K4V_DEV void store_coherent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-Q8K4V_DEV float load_coherent(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int D>
 constexpr int partial_stride() { return D + 4; }   // m, l, pad, pad, o[D]
 
@@ -128,9 +117,9 @@ Q8K4V_DEV void write_zero_rows(const AttnParams& p, const WorkItem& w, int r0, i
 
 // Log-sum-exp merge of the n_eff split partials of (b, kh) for rows
 // [r0, r0 + NR), by the threads of the last workgroup to finish.  The split
-// records were written with write-through stores by workgroups on any XCD;
-// an agent-scope acquire (which invalidates this XCD's L2) lets plain,
-// vectorised loads see them.  Thread t takes (row, float4 column) pairs and
+// records were written by workgroups on any XCD and released by their
+// arrivals (fused_tail); an agent-scope acquire (which drops this XCD's stale
+// L2 lines) lets plain, vectorised loads see them.  Thread t takes (row, float4 column) pairs and
 // a split group, loads the records of its splits in batches of CH with all
 // loads of a batch in flight, merges them online, and the split groups are
 // merged through LDS.  Every load of a batch is unconditional (split index
@@ -232,24 +221,30 @@ Q8K4V_DEV void emit_element(const AttnParams& p, const WorkItem& w, int r, int d
         const size_t rs = (size_t)p.R * partial_stride<D>();
         float* rec = p.partials + ((size_t)w.b * p.H + w.kh) * p.n_splits * rs + w.split * rs +
                      (size_t)r * partial_stride<D>();
-        if (d == 0) { store_coherent(rec, M); store_coherent(rec + 1, Ls); }
-        store_coherent(rec + 4 + d, O);
+        if (d == 0) *(float2*)rec = float2{M, Ls};
+        rec[4 + d] = O;
     }
 }
 
 // With the fused combine, the last workgroup of (b, kh, row chunk) to finish
-// merges all splits.  Called by every thread after its emit_element calls.
+// merges all splits.  Called by every thread after its record stores.  The
+// records cross XCDs (each XCD has its own L2): every wave waits for its
+// stores, the barrier orders them before thread 0's arrival, and the
+// arrival is an agent-scope acquire-release read-modify-write -- its release
+// writes this XCD's dirty L2 lines back, its acquire (and the merging
+// threads' acquire fence) drops stale lines -- so the merge's plain loads
+// see every record.  The last arrival resets the counter to zero: between
+// completed calls every counter of the workspace header is zero.
 template <int D, int RW>
 Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0, void* scratch, int scratch_bytes) {
     if (p.direct || !p.fused) return;
     __shared__ int s_last;
     const int n_eff = (max(0, w.npages - p.page_lo) + p.split_pages - 1) / p.split_pages;
-    // every thread's write-through stores have completed before the barrier
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t* ctr = p.counters + ((size_t)w.b * p.H + w.kh) * p.row_chunks + w.rchunk;
-        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1 == (uint32_t)n_eff);
         if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -261,9 +256,9 @@ Q8K4V_DEV void fused_tail(const AttnParams& p, const WorkItem& w, int r0, void* 
 // Emit the merged rows [r0, r0 + RW) of a workgroup, four dimensions per
 // thread: s_M / s_L hold each row's max and sum, s_o [RW][SO_STRIDE] its unnormalised
 // output (already on the row's reference).  One split: the normalised output.
-// Several: the split record (m, l, o), with plain stores when a separate
-// combine kernel reads it (the kernel boundary orders them) and write-through
-// stores when the last workgroup merges in this launch.
+// Several: the split record (m, l, o); a separate combine kernel reads it
+// after the kernel boundary, the in-launch merge after fused_tail's
+// acquire-release arrival.
 template <int D, int RW, int SO_STRIDE = D>
 Q8K4V_DEV void emit_rows(const AttnParams& p, const WorkItem& w, int r0, const float* s_M, const float* s_L,
                          const float* s_o) {
@@ -282,16 +277,8 @@ Q8K4V_DEV void emit_rows(const AttnParams& p, const WorkItem& w, int r0, const f
             continue;
         }
         float* rec = split_base + (size_t)r * partial_stride<D>();
-        if (p.fused) {
-            if (qc == 0) { store_coherent(rec, s_M[rl]); store_coherent(rec + 1, Ls); }
-            store_coherent(rec + 4 + 4 * qc, O.x);
-            store_coherent(rec + 5 + 4 * qc, O.y);
-            store_coherent(rec + 6 + 4 * qc, O.z);
-            store_coherent(rec + 7 + 4 * qc, O.w);
-        } else {
-            if (qc == 0) *(float2*)rec = float2{s_M[rl], Ls};
-            *((f32x4*)(rec + 4) + qc) = O;
-        }
+        if (qc == 0) *(float2*)rec = float2{s_M[rl], Ls};
+        *((f32x4*)(rec + 4) + qc) = O;
     }
 }
 

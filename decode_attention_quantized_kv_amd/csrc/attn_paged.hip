@@ -133,6 +133,62 @@ Q8K4V_DEV void value_zero_pairs(const uint32_t* vz0, const uint32_t* vz1, int g,
     }
 }
 
+// The query row as the int8 B operands of q.K.  Each value x becomes a 23-bit
+// fixed-point number Q = rne(x * 2^(22 - e)) with 2^(e-1) <= max|row| < 2^e,
+// so |Q| <= 2^22 and the rounding error of an element is at most 2^(e-23) <=
+// max|row| * 2^-22 (a bf16 element within 2^15 of the row's largest
+// magnitude is exact).  Q is written in base-256 signed digits
+// Q = 65536 h + 256 m + l (l, m in -128..127, h in -64..64): three int8
+// operands whose int32 MFMA sums are exact.  One fma against 1.5 * 2^23
+// rounds x * 2^(22-e) to an integer, ties to even, inside the fp32 mantissa
+// (bits = 0x4B400000 + Q); W = Q + 128 * (65536 + 256 + 1) lies in 0 .. 2^24
+// and byte k of W is digit k + 128, so digit k as int8 is byte k XOR 0x80.
+// Byte t of word c holds element 4c + t (the MFMA B layout of one lane).
+struct QDigits { u32x4 h, m, l; };
+
+template <bool SUM>
+Q8K4V_DEV QDigits query_digits(const float (&x)[16], float sc, int& qsum) {
+    uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        uint32_t W[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            W[t] = fbits(__builtin_fmaf(x[4 * c + t], sc, 12582912.0f)) - 1254064000u;
+            if (SUM) qsum += (int)W[t] - 8421504;            // Q
+        }
+        const uint32_t a01 = __builtin_amdgcn_perm(W[1], W[0], 0x05040100u);   // bytes 0, 1 of W0, W1
+        const uint32_t a23 = __builtin_amdgcn_perm(W[3], W[2], 0x05040100u);
+        const uint32_t b01 = __builtin_amdgcn_perm(W[1], W[0], 0x07060302u);   // bytes 2, 3 of W0, W1
+        const uint32_t b23 = __builtin_amdgcn_perm(W[3], W[2], 0x07060302u);
+        lw[c] = __builtin_amdgcn_perm(a23, a01, 0x06040200u) ^ 0x80808080u;
+        mw[c] = __builtin_amdgcn_perm(a23, a01, 0x07050301u) ^ 0x80808080u;
+        hw[c] = __builtin_amdgcn_perm(b23, b01, 0x06040200u) ^ 0x80808080u;
+    }
+    return QDigits{u32x4{hw[0], hw[1], hw[2], hw[3]}, u32x4{mw[0], mw[1], mw[2], mw[3]},
+                   u32x4{lw[0], lw[1], lw[2], lw[3]}};
+}
+
+// Exponent e of a row maximum (2^(e-1) <= mx < 2^e), clamped so that
+// 2^(22-e) and 2^(e-22) stay normal fp32 numbers; rows with max|q| >= 2^100
+// are outside the supported range.
+Q8K4V_DEV int row_exponent(float mx) {
+    int e = 0;
+    if (mx > 0.0f) (void)frexpf(mx, &e);
+    return min(max(e, -100), 100);
+}
+
+// Score of one token from the three digit sums: Q.c = 65536 H + 256 M + L,
+// formed as fp32 (65536 H + 256 M is exact in int32; the fp32 result carries
+// a relative rounding error of at most 2^-23).  Affine keys subtract the
+// key zero point times the row's sum of Q.
+template <bool AFF>
+Q8K4V_DEV float digit_dot(int H, int M, int L, int zp, float qsumf) {
+    float f = __builtin_fmaf((float)(H * 256 + M), 256.0f, (float)L);
+    if (AFF) f = __builtin_fmaf(-(float)zp, qsumf, f);
+    return f;
+}
+
 // The kernel bodies take their tile ring (WAVES x STAGES stages, in LDS) and
 // their block index as arguments so that one launch can run two of them
 // (the shared-prefix cascade's fused pass).
@@ -241,21 +297,19 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
             }
         }
     };
-    // ---- query row (n mod R) as the B operand: 15-bit fixed point
-    // Q = rne(q * 2^(14-e)) (2^(e-1) <= max|q_row| < 2^e), int8 halves
-    // hi = (Q + 128) >> 8, lo = Q - 256 hi; lane (n, q) holds dims
-    // 64 ks + 16 q .. +15 of every k-step ks
+    // ---- query row (n mod R) as the B operands (query_digits); lane (n, q)
+    // holds dims 64 ks + 16 q .. +15 of every k-step ks
     // (the query loads go out with the page-id load, before the first
     // copies: the compiler's wait for them then covers no copy)
     // (SQ: wave 0 converts and hands the operands to the other waves through
     // LDS; those start their first copies at once)
-    u32x4 qhi[KS], qlo[KS];
+    QDigits qd[KS];
     float coef;
-    int qsum = 0;                              // sum of the row's fixed-point Q (affine keys)
+    float qsumf = 0.0f;                        // sum of the row's fixed-point Q (affine keys)
     const int lim = w.L - p.W + 1 + row / p.G;
-    __shared__ u32x4 s_q[SQ ? KS * 2 * 64 : 1];
+    __shared__ u32x4 s_q[SQ ? KS * 3 * 64 : 1];
     __shared__ float s_coef[SQ ? 64 : 1];
-    __shared__ int s_qsum[SQ ? 64 : 1];
+    __shared__ float s_qsum[SQ ? 64 : 1];
     if (SQ && wave != 0) {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
@@ -294,54 +348,34 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < nt) issue(s, s);
-        int e = 0;
-        if (mx > 0.0f) (void)frexpf(mx, &e);
-        e = min(max(e, -110), 110);
-        const float sc = ldexpf(1.0f, 14 - e);
-        // U = Q + 128 by one fma against 1.5 * 2^23 + 128: |Q| <= 2^14, so the
-        // sum's low 16 bits are U (round-half-even like rintf); then
-        // hi byte = U >> 8, lo byte = (U & 0xFF) - 128 = (U ^ 0x80) & 0xFF
+        const int e = row_exponent(mx);
+        const float sc = ldexpf(1.0f, 22 - e);
+        int qsum = 0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                uint32_t u[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) u[t] = fbits(__builtin_fmaf(x[ks][4 * c + t], sc, 12583040.0f));
-                if (AFF) {                     // Q = (int16) U - 128
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) qsum += (int)(int16_t)(u[t] & 0xFFFFu) - 128;
-                }
-                const uint32_t u01 = __builtin_amdgcn_perm(u[1], u[0], 0x05040100u);   // U0 | U1 << 16
-                const uint32_t u23 = __builtin_amdgcn_perm(u[3], u[2], 0x05040100u);
-                hw[c] = __builtin_amdgcn_perm(u23, u01, 0x07050301u);                 // byte 1 of U0..U3
-                lw[c] = __builtin_amdgcn_perm(u23, u01, 0x06040200u) ^ 0x80808080u;   // byte 0 of U0..U3
-            }
-            qhi[ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-            qlo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-        }
-        coef = p.scale_log2 * ldexpf(1.0f, e - 14);
-        if (AFF) qsum = xgroups_isum(qsum);
+        for (int ks = 0; ks < KS; ++ks) qd[ks] = query_digits<AFF>(x[ks], sc, qsum);
+        coef = p.scale_log2 * ldexpf(1.0f, e - 22);
+        if (AFF) qsumf = (float)xgroups_isum(qsum);
         if (SQ) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                s_q[(2 * ks) * 64 + lane] = qhi[ks];
-                s_q[(2 * ks + 1) * 64 + lane] = qlo[ks];
+                s_q[(3 * ks) * 64 + lane] = qd[ks].h;
+                s_q[(3 * ks + 1) * 64 + lane] = qd[ks].m;
+                s_q[(3 * ks + 2) * 64 + lane] = qd[ks].l;
             }
             s_coef[lane] = coef;
-            s_qsum[lane] = qsum;
+            s_qsum[lane] = qsumf;
         }
     }
     if (SQ) {
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            qhi[ks] = s_q[(2 * ks) * 64 + lane];
-            qlo[ks] = s_q[(2 * ks + 1) * 64 + lane];
+            qd[ks].h = s_q[(3 * ks) * 64 + lane];
+            qd[ks].m = s_q[(3 * ks + 1) * 64 + lane];
+            qd[ks].l = s_q[(3 * ks + 2) * 64 + lane];
         }
         coef = s_coef[lane];
-        qsum = s_qsum[lane];
+        qsumf = s_qsum[lane];
     }
     // APP: codes and scales (affine: and zero points) of the new token, by
     // the append kernel's rule; affine key codes and zero point are stored
@@ -470,17 +504,17 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
         }
         wait_lds_all();
 
-        // ---- scores
-        i32x4_t chi[TP], clo[TP];
+        // ---- scores: three digit chains per page
+        i32x4_t ch[TP], cm[TP], cl[TP];
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
-            chi[u] = i32x4_t{0, 0, 0, 0};
-            clo[u] = i32x4_t{0, 0, 0, 0};
+            ch[u] = cm[u] = cl[u] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const i32x4_t a = __builtin_bit_cast(i32x4_t, ka[u][ks]);
-                chi[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qhi[ks]), chi[u], 0, 0, 0);
-                clo[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qlo[ks]), clo[u], 0, 0, 0);
+                ch[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qd[ks].h), ch[u], 0, 0, 0);
+                cm[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qd[ks].m), cm[u], 0, 0, 0);
+                cl[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qd[ks].l), cl[u], 0, 0, 0);
             }
         }
         const int pg0 = w.pbeg + TP * (wave + WAVES * t);
@@ -490,11 +524,9 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
             const float kf[4] = {h2f((uint16_t)ksw[u].x), h2f((uint16_t)(ksw[u].x >> 16)), h2f((uint16_t)ksw[u].y),
                                  h2f((uint16_t)(ksw[u].y >> 16))};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int dot = 256 * chi[u][i] + clo[u][i];
-                if (AFF) dot -= (int)(int8_t)(kzw[u] >> (8 * i)) * qsum;   // q.(c - z) in fixed point
-                s[u][i] = (float)dot * (kf[i] * coef);
-            }
+            for (int i = 0; i < 4; ++i)
+                s[u][i] = digit_dot<AFF>(ch[u][i], cm[u][i], cl[u][i], (int8_t)(kzw[u] >> (8 * i)), qsumf) *
+                          (kf[i] * coef);
         }
         if ((pg0 + TP) * 16 > lim_min || pg0 + TP > pend) {      // tile reaches the causal edge / split end
 #pragma unroll
@@ -601,7 +633,7 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
 template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_dec2_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
-    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + (D / 64) * 2048 + 8192 <= 163840;
+    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + (D / 64) * 3072 + 8192 <= 163840;
     dec2_body<D, R, WAVES, STAGES, QBF16, AFF, false, SQ>(p, s_stage, (int)blockIdx.x);
 }
 
@@ -699,18 +731,18 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
         }
     };
 
-    // ---- query rows r0 + 16 rb + n as B operands (15-bit fixed point, int8
-    // halves; rows past R are zero).  SQ: wave rb converts row block rb only
+    // ---- query rows r0 + 16 rb + n as B operands (query_digits; rows past R
+    // are zero).  SQ: wave rb converts row block rb only
     // and hands it to the others through LDS; the other waves start their
     // first copies at once.
-    u32x4 qhi[RB][KS], qlo[RB][KS];
+    QDigits qd[RB][KS];
     float coef[RB];
     int lim[RB];
-    int qsum[RB];                              // sum of each row's fixed-point Q (affine keys)
+    float qsumf[RB];                           // sum of each row's fixed-point Q (affine keys)
     static_assert(!SQ || WAVES >= RB, "one converting wave per row block");
-    __shared__ u32x4 s_q[SQ ? RB * KS * 2 * 64 : 1];
+    __shared__ u32x4 s_q[SQ ? RB * KS * 3 * 64 : 1];
     __shared__ float s_coef[SQ ? RB * 16 : 1];
-    __shared__ int s_qsum[SQ ? RB * 16 : 1];
+    __shared__ float s_qsum[SQ ? RB * 16 : 1];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int r = r0 + 16 * rb + n16;
@@ -770,42 +802,23 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             if (SQ && rb != wave) continue;
-            int e = 0;
-            if (mx[rb] > 0.0f) (void)frexpf(mx[rb], &e);
-            e = min(max(e, -110), 110);
-            const float sc = ldexpf(1.0f, 14 - e);
+            const int e = row_exponent(mx[rb]);
+            const float sc = ldexpf(1.0f, 22 - e);
             int qs = 0;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    uint32_t u[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) u[t] = fbits(__builtin_fmaf(x[rb][ks][4 * c + t], sc, 12583040.0f));
-                    if (AFF) {                 // Q = (int16) U - 128
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) qs += (int)(int16_t)(u[t] & 0xFFFFu) - 128;
-                    }
-                    const uint32_t u01 = __builtin_amdgcn_perm(u[1], u[0], 0x05040100u);
-                    const uint32_t u23 = __builtin_amdgcn_perm(u[3], u[2], 0x05040100u);
-                    hw[c] = __builtin_amdgcn_perm(u23, u01, 0x07050301u);
-                    lw[c] = __builtin_amdgcn_perm(u23, u01, 0x06040200u) ^ 0x80808080u;
-                }
-                qhi[rb][ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-                qlo[rb][ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            }
-            coef[rb] = p.scale_log2 * ldexpf(1.0f, e - 14);
-            qsum[rb] = AFF ? xgroups_isum(qs) : 0;
+            for (int ks = 0; ks < KS; ++ks) qd[rb][ks] = query_digits<AFF>(x[rb][ks], sc, qs);
+            coef[rb] = p.scale_log2 * ldexpf(1.0f, e - 22);
+            qsumf[rb] = AFF ? (float)xgroups_isum(qs) : 0.0f;
             if (SQ) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    s_q[((rb * KS + ks) * 2) * 64 + lane] = qhi[rb][ks];
-                    s_q[((rb * KS + ks) * 2 + 1) * 64 + lane] = qlo[rb][ks];
+                    s_q[((rb * KS + ks) * 3) * 64 + lane] = qd[rb][ks].h;
+                    s_q[((rb * KS + ks) * 3 + 1) * 64 + lane] = qd[rb][ks].m;
+                    s_q[((rb * KS + ks) * 3 + 2) * 64 + lane] = qd[rb][ks].l;
                 }
                 if (q4 == 0) {
                     s_coef[rb * 16 + n16] = coef[rb];
-                    s_qsum[rb * 16 + n16] = qsum[rb];
+                    s_qsum[rb * 16 + n16] = qsumf[rb];
                 }
             }
         }
@@ -816,11 +829,12 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
         for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                qhi[rb][ks] = s_q[((rb * KS + ks) * 2) * 64 + lane];
-                qlo[rb][ks] = s_q[((rb * KS + ks) * 2 + 1) * 64 + lane];
+                qd[rb][ks].h = s_q[((rb * KS + ks) * 3) * 64 + lane];
+                qd[rb][ks].m = s_q[((rb * KS + ks) * 3 + 1) * 64 + lane];
+                qd[rb][ks].l = s_q[((rb * KS + ks) * 3 + 2) * 64 + lane];
             }
             coef[rb] = s_coef[rb * 16 + n16];
-            qsum[rb] = s_qsum[rb * 16 + n16];
+            qsumf[rb] = s_qsum[rb * 16 + n16];
         }
     }
     const int lim_min = w.L - p.W + 1;
@@ -888,19 +902,19 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
         }
         wait_lds_all();
 
-        // ---- scores
-        i32x4_t chi[RB][TP], clo[RB][TP];
+        // ---- scores: three digit chains per page and row block
+        i32x4_t ch[RB][TP], cm[RB][TP], cl[RB][TP];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int u = 0; u < TP; ++u) {
-                chi[rb][u] = i32x4_t{0, 0, 0, 0};
-                clo[rb][u] = i32x4_t{0, 0, 0, 0};
+                ch[rb][u] = cm[rb][u] = cl[rb][u] = i32x4_t{0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const i32x4_t a = __builtin_bit_cast(i32x4_t, ka[u][ks]);
-                    chi[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qhi[rb][ks]), chi[rb][u], 0, 0, 0);
-                    clo[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qlo[rb][ks]), clo[rb][u], 0, 0, 0);
+                    ch[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qd[rb][ks].h), ch[rb][u], 0, 0, 0);
+                    cm[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qd[rb][ks].m), cm[rb][u], 0, 0, 0);
+                    cl[rb][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, __builtin_bit_cast(i32x4_t, qd[rb][ks].l), cl[rb][u], 0, 0, 0);
                 }
             }
         const int pg0 = w.pbeg + TP * (wave + WAVES * t);
@@ -921,11 +935,9 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
             for (int u = 0; u < TP; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    int dot = 256 * chi[rb][u][i] + clo[rb][u][i];
-                    if (AFF) dot -= (int)(int8_t)(kzw[u] >> (8 * i)) * qsum[rb];   // q.(c - z) in fixed point
-                    s[u][i] = (float)dot * (kf[u][i] * coef[rb]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    s[u][i] = digit_dot<AFF>(ch[rb][u][i], cm[rb][u][i], cl[rb][u][i], (int8_t)(kzw[u] >> (8 * i)),
+                                             qsumf[rb]) * (kf[u][i] * coef[rb]);
             if (edge) {
 #pragma unroll
                 for (int u = 0; u < TP; ++u)
@@ -1081,13 +1093,8 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                 continue;
             }
             float* rec = split_base + (size_t)r * partial_stride<D>();
-            if (p.fused) {
-                if (d == 0) { store_coherent(rec, s_M[rl]); store_coherent(rec + 1, Ls); }
-                store_coherent(rec + 4 + d, ov[k]);
-            } else {
-                if (d == 0) *(float2*)rec = float2{s_M[rl], Ls};
-                rec[4 + d] = ov[k];
-            }
+            if (d == 0) *(float2*)rec = float2{s_M[rl], Ls};
+            rec[4 + d] = ov[k];
         }
     }
     fused_tail<D, RW>(p, w, r0, smem, WAVES * STAGES * STAGE);
@@ -1096,9 +1103,9 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
-    // the shared query operands (RB x 2 KiB per 64 dimensions) where the LDS
+    // the shared query operands (RB x 3 KiB per 64 dimensions) where the LDS
     // budget allows them
-    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + RB * (D / 64) * 2048 + 8192 <= 163840;
+    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + RB * (D / 64) * 3072 + 8192 <= 163840;
     rows_body<D, RB, WAVES, STAGES, QBF16, AFF, SQ>(p, s_stage, (int)blockIdx.x);
 }
 

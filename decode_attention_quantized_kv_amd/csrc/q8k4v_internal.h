@@ -46,16 +46,17 @@ struct AttnArgs {
     float softmax_scale;
 };
 
-enum Kernel { kVector = 1, kBlockMfma = 2, kMfma = 3, kDec2 = 4, kRows = 5 };
+// The two attention kernels of attn_paged.hip, numbered as the `variant`
+// field of q8k4v_config selects them.
+enum Kernel { kDec2 = 4, kRows = 5 };
 
 // Fully resolved launch plan.
 struct Plan {
     int32_t rows;          // query rows per kv head = n_draft * group
     int32_t kernel;        // Kernel
-    int32_t mfma;          // 1: the unit is the dense-MFMA one (more than 8 rows)
     int32_t tile_pages;
     int32_t waves;
-    int32_t stages;        // tile buffers per wave (kDec2)
+    int32_t stages;        // tile buffers per wave in the LDS ring
     int32_t rows_per_wg;   // rows handled by one workgroup (row chunk)
     int32_t row_chunks;    // workgroups per (sequence, kv head, split) along rows
     int32_t split_pages;   // pages per workgroup
@@ -74,6 +75,10 @@ q8k4v_config default_config(int32_t rows);
 int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg, Plan* plan);
 size_t plan_workspace(const Plan& p);
 
+// Arrival counters of the in-launch merge: one uint32 per (sequence, kv
+// head, row chunk) at the front of the workspace header.
+constexpr int64_t kMaxCounters = Q8K4V_WS_HEADER_BYTES / sizeof(uint32_t);
+
 int32_t launch_attention(const AttnArgs& a, const Plan& plan, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
 
@@ -86,6 +91,7 @@ struct CascadePlan {
 constexpr int32_t kMaxPrefixRows = 4096;
 constexpr int32_t kCascadeSuffixWgsPerCu = 4;   // suffix pass, when the caller gives no config
 int32_t make_cascade_plan(const AttnArgs& a, int32_t n_prefix_pages, const q8k4v_config* cfg, CascadePlan* cp);
+size_t cascade_workspace(const CascadePlan& cp);
 int32_t launch_cascade(const AttnArgs& a, int32_t n_prefix_pages, const CascadePlan& cp, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 

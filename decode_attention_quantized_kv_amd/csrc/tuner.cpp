@@ -31,11 +31,15 @@
 // (architecture, device name and CU count, HIP runtime and driver versions,
 // library build) and request shape; a later call with the same identity and
 // shape uses the stored choice without measuring, and a changed identity
-// (new driver, toolchain or library) searches again.  Admission: on each of the unit's two shapes, the candidate's
-// output may differ from the default configuration's output by at most
-// alpha = 8 times the storage-resolution noise -- the change of the default
-// output when every stored code moves by one quantisation step -- and, when
-// the caller passes reference outputs, by at most ref_tol from them.
+// (new driver, toolchain or library) searches again.  Admission: on each of
+// the unit's two shapes, the candidate's output may differ from the default
+// configuration's output by at most alpha = 8 times the storage-resolution
+// noise -- the change of the default output when every stored code moves by
+// one quantisation step -- and, on every term for which the caller passes a
+// reference output (decode and verify at both contexts, e.g. computed by a
+// CPU oracle on the caller's inputs), the sigma-normalised deviation from it
+// may not exceed ref_tol.  A deviation that was not measured is reported as
+// unknown (null), never as 0.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -138,15 +142,18 @@ struct Shape {
     bool small;
 };
 
+constexpr double kUnmeasured = NAN;   // printed as null ("unknown")
+
 struct Cand {
     q8k4v_config cfg;
     std::string stage;             // "default", "structural", "refine"
     std::string verdict;           // "admitted", "rejected", "invalid", "unknown"
+    std::string gate;              // rejected by: "alpha" or "oracle"
     std::string why;
-    double t[2] = {0, 0};          // median microseconds per shape
-    double dev[2] = {0, 0};        // max |out - default out| per shape
-    double ref_dev = -1;
-    double cost = 0;
+    double t[2] = {kUnmeasured, kUnmeasured};     // median microseconds per shape
+    double dev[2] = {kUnmeasured, kUnmeasured};   // max |out - default out| per shape
+    double ref_dev[2] = {kUnmeasured, kUnmeasured};   // normalised deviation from the unit's references
+    double cost = kUnmeasured;
     int seq = -1;                  // position in the measurement order (both units)
     double vt[2] = {-1, -1};       // virtual completion times of the units when it was picked
 };
@@ -190,6 +197,13 @@ bool same_cfg(const q8k4v_config& a, const q8k4v_config& b) {
            a.split_pages == b.split_pages && a.fused_combine == b.fused_combine && a.stages == b.stages;
 }
 
+// Text safe inside a JSON string (quotes, backslashes and controls blanked).
+std::string json_text(std::string w) {
+    for (auto& ch : w)
+        if (ch == '"' || ch == '\\' || (unsigned char)ch < 32) ch = ' ';
+    return w;
+}
+
 std::string fmt(double x) {
     if (!std::isfinite(x)) return "null";     // JSON has no inf / nan
     char b[64];
@@ -210,7 +224,9 @@ class Tuner {
     int32_t launch(const q8k4v_config* cfg, const Shape& s, int copy, int set, float* out, const void* q);
     int32_t time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us);
     int32_t output(const q8k4v_config* cfg, const Shape& s, int copy, std::vector<float>* host);
-    int32_t ref_output(const q8k4v_config* cfg, bool verify, std::vector<float>* host);
+    int32_t ref_output(const q8k4v_config* cfg, int term, std::vector<float>* host);
+    bool has_ref(int term) const { return req_.ref[term].cache != nullptr; }
+    double ref_deviation(int term, const std::vector<float>& o) const;
     void start_unit(int unit, UnitSearch* u);
     void refine_queue(int unit, UnitSearch* u);
     void measure(int unit, Cand* c);
@@ -227,7 +243,7 @@ class Tuner {
     std::vector<q8k4v_cache> copies_;
     int32_t* d_tables_ = nullptr;        // [n_sets][pages]: set 0 is the full permutation
     int32_t* d_lens_ = nullptr;          // [4]: decode small, decode large, verify small, verify large
-    int32_t* d_ref_len_ = nullptr;       // [1]: the caller's reference length
+    int32_t* d_ref_lens_ = nullptr;      // [4]: the caller's reference lengths per term
     void* d_q_ = nullptr;                // bf16 [w][hq][d]
     float* d_out_ = nullptr;             // fp32 [w][hq][d]
     void* d_ws_ = nullptr;
@@ -236,7 +252,6 @@ class Tuner {
     std::vector<float> def_out_[2][2];   // default outputs per unit/shape on copy 0
     double noise_[2][2] = {{0, 0}, {0, 0}};
     double def_t_[2][2] = {{0, 0}, {0, 0}};
-    std::vector<float> ref_host_[2];
     std::string setup_note_;
     int seq_ = 0;                        // measurement order over both units
     std::string summary_, error_;
@@ -269,10 +284,13 @@ int32_t Tuner::setup(std::string* why) {
     // workspace: the largest any candidate can ask for (split count is capped
     // by the combine, so the bound is the cap times the row records)
     ws_bytes_ = 0;
+    int max_len = ctx_l + w_;
+    for (int k = 0; k < 4; ++k)
+        if (has_ref(k)) max_len = std::max(max_len, req_.ref[k].len);
     for (int unit = 0; unit < 2; ++unit)
-        for (int wgs : {1, 2, 3, 4, 5, 6, 8, 12})
-            for (int waves : {1, 2, 4})
-                for (int variant : {0, 1, 2, 3, 4}) {
+        for (int wgs : {1, 2, 3, 4, 6})
+            for (int waves : {2, 4, 8})
+                for (int variant : {0, 4, 5}) {
                     q8k4v_config c = default_config(rows_of(unit));
                     c.wgs_per_cu = wgs;
                     c.waves_per_wg = waves;
@@ -280,9 +298,9 @@ int32_t Tuner::setup(std::string* why) {
                     c.stages = 0;
                     c.fused_combine = 1;
                     const int nd = unit ? w_ : 1;
-                    ws_bytes_ = std::max(ws_bytes_, q8k4v_workspace_bytes(1, hq_, h_, d_, ctx_l + w_, nd, &c));
+                    ws_bytes_ = std::max(ws_bytes_, q8k4v_workspace_bytes(1, hq_, h_, d_, max_len, nd, &c));
                 }
-    ws_bytes_ = std::max<size_t>(ws_bytes_, 4096);
+    ws_bytes_ = std::max<size_t>(ws_bytes_, Q8K4V_WS_HEADER_BYTES);
 
     size_t free_b = 0, total_b = 0;
     if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: hipMemGetInfo");
@@ -344,21 +362,26 @@ int32_t Tuner::setup(std::string* why) {
             tables[(size_t)set * pages_ + i] = perm[(i + (size_t)set * small_pages_) % pages_];
     d_tables_ = (int32_t*)arena_.alloc(tables.size() * 4);
     d_lens_ = (int32_t*)arena_.alloc(16);
+    d_ref_lens_ = (int32_t*)arena_.alloc(16);
     d_q_ = arena_.alloc((size_t)w_ * hq_ * d_ * 2);
     d_out_ = (float*)arena_.alloc((size_t)w_ * hq_ * d_ * 4);
     d_ws_ = arena_.alloc(ws_bytes_);
-    if (!d_tables_ || !d_lens_ || !d_q_ || !d_out_ || !d_ws_) {
+    if (!d_tables_ || !d_lens_ || !d_ref_lens_ || !d_q_ || !d_out_ || !d_ws_) {
         *why = "hipMalloc failed";
         return Q8K4V_ENOMEM;
     }
     const int32_t lens[4] = {shapes_[0][0].ctx, shapes_[0][1].ctx, shapes_[1][0].ctx, shapes_[1][1].ctx};
+    const int32_t ref_lens[4] = {req_.ref[0].len, req_.ref[1].len, req_.ref[2].len, req_.ref[3].len};
     if (hipMemcpyAsync(d_tables_, tables.data(), tables.size() * 4, hipMemcpyHostToDevice, stream_) != hipSuccess ||
-        hipMemcpyAsync(d_lens_, lens, sizeof lens, hipMemcpyHostToDevice, stream_) != hipSuccess)
+        hipMemcpyAsync(d_lens_, lens, sizeof lens, hipMemcpyHostToDevice, stream_) != hipSuccess ||
+        hipMemcpyAsync(d_ref_lens_, ref_lens, sizeof ref_lens, hipMemcpyHostToDevice, stream_) != hipSuccess)
         return hip_fail(hipGetLastError(), "tune_select: upload");
     hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream_, (uint16_t*)d_q_, (size_t)w_ * hq_ * d_,
                        req_.seed ^ 0xA11CEULL);
-    // the fused combine's counters start at zero and reset themselves
-    if (hipMemsetAsync(d_ws_, 0, ws_bytes_, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
+    // the workspace header (the in-launch merge's counters) starts at zero;
+    // every completed launch leaves it at zero, whatever its plan
+    if (hipMemsetAsync(d_ws_, 0, Q8K4V_WS_HEADER_BYTES, stream_) != hipSuccess)
+        return hip_fail(hipGetLastError(), "tune_select: memset");
     if (hipStreamSynchronize(stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: synthesis");
     reps_ = 5;
     events_.resize(2 * reps_);
@@ -434,30 +457,41 @@ int32_t Tuner::output(const q8k4v_config* cfg, const Shape& s, int copy, std::ve
     return Q8K4V_OK;
 }
 
-int32_t Tuner::ref_output(const q8k4v_config* cfg, bool verify, std::vector<float>* host) {
+// Output of a candidate on reference term `term` (0, 1 decode; 2, 3 verify).
+int32_t Tuner::ref_output(const q8k4v_config* cfg, int term, std::vector<float>* host) {
+    const q8k4v_tune_ref& r = req_.ref[term];
+    const bool verify = term >= 2;
     const int nd = verify ? w_ : 1;
     const size_t n = (size_t)nd * hq_ * d_;
-    const int32_t len = req_.ref_len;
-    if (!d_ref_len_) {
-        d_ref_len_ = (int32_t*)arena_.alloc(4);
-        if (!d_ref_len_) return fail(Q8K4V_ENOMEM, "tune_select: hipMalloc");
-        if (hipMemcpyAsync(d_ref_len_, &len, 4, hipMemcpyHostToDevice, stream_) != hipSuccess ||
-            hipStreamSynchronize(stream_) != hipSuccess)
-            return hip_fail(hipGetLastError(), "tune_select: upload");
-    }
     int32_t rc;
+    if (hipMemsetAsync(d_out_, 0xFF, n * 4, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
     if (verify)
-        rc = attn_verify_q8k4v(req_.ref_cache, req_.ref_q_verify, Q8K4V_BF16, d_out_, 1, hq_, nd, d_ref_len_, len,
-                               req_.ref_page_table, req_.ref_max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
+        rc = attn_verify_q8k4v(r.cache, r.q, Q8K4V_BF16, d_out_, 1, hq_, nd, d_ref_lens_ + term, r.len, r.page_table,
+                               r.max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
     else
-        rc = attn_decode_q8k4v(req_.ref_cache, req_.ref_q, Q8K4V_BF16, d_out_, 1, hq_, d_ref_len_, len,
-                               req_.ref_page_table, req_.ref_max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
+        rc = attn_decode_q8k4v(r.cache, r.q, Q8K4V_BF16, d_out_, 1, hq_, d_ref_lens_ + term, r.len, r.page_table,
+                               r.max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
     if (rc != Q8K4V_OK) return rc;
     host->resize(n);
     if (hipMemcpyAsync(host->data(), d_out_, n * 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipStreamSynchronize(stream_) != hipSuccess)
         return hip_fail(hipGetLastError(), "tune_select: readback");
     return Q8K4V_OK;
+}
+
+// max over elements of |o - ref| / sigma (sigma per (q head, dim), 1 if not
+// given); a non-finite output gives +inf.
+double Tuner::ref_deviation(int term, const std::vector<float>& o) const {
+    const float* ref = req_.ref[term].out;
+    const float* sigma = req_.ref[term].sigma;
+    const size_t hd = (size_t)hq_ * d_;
+    double m = 0;
+    for (size_t i = 0; i < o.size(); ++i) {
+        const double sig = sigma ? (double)sigma[i % hd] : 1.0;
+        const double d = std::fabs((double)o[i] - (double)ref[i]) / sig;
+        if (!(d <= m)) m = std::isnan(d) ? INFINITY : d;
+    }
+    return m;
 }
 
 double max_abs_diff(const std::vector<float>& a, const float* b, size_t n) {
@@ -470,7 +504,9 @@ double max_abs_diff(const std::vector<float>& a, const float* b, size_t n) {
 }
 
 void Tuner::measure(int unit, Cand* c) {
-    // timing on both shapes, then the gate; "unknown" if the deadline passes
+    // timing on both shapes, then the alpha gate on both shapes, then the
+    // oracle gate on the unit's reference terms; "unknown" if the deadline
+    // passes first (what was not measured stays unknown)
     for (int k = 0; k < 2; ++k) {
         if (expired()) { c->verdict = "unknown"; c->why = "deadline"; return; }
         const int32_t rc = time_shape(&c->cfg, shapes_[unit][k], &c->t[k]);
@@ -484,20 +520,24 @@ void Tuner::measure(int unit, Cand* c) {
         c->dev[k] = max_abs_diff(def_out_[unit][k], o.data(), o.size());
         if (!(c->dev[k] <= kAlpha * noise_[unit][k])) {
             c->verdict = "rejected";
+            c->gate = "alpha";
             c->why = shapes_[unit][k].name + ": deviation " + fmt(c->dev[k]) + " > alpha * noise " +
                      fmt(kAlpha * noise_[unit][k]);
             return;
         }
     }
-    if (!ref_host_[unit].empty()) {
+    for (int k = 0; k < 2; ++k) {
+        const int term = 2 * unit + k;
+        if (!has_ref(term)) continue;
         if (expired()) { c->verdict = "unknown"; c->why = "deadline"; return; }
         std::vector<float> o;
-        const int32_t rc = ref_output(&c->cfg, unit == 1, &o);
+        const int32_t rc = ref_output(&c->cfg, term, &o);
         if (rc != Q8K4V_OK) { c->verdict = "invalid"; c->why = q8k4v_last_error(); return; }
-        c->ref_dev = max_abs_diff(o, ref_host_[unit].data(), o.size());
-        if (!(c->ref_dev <= req_.ref_tol)) {
+        c->ref_dev[k] = ref_deviation(term, o);
+        if (!(c->ref_dev[k] <= req_.ref_tol)) {
             c->verdict = "rejected";
-            c->why = "reference deviation " + fmt(c->ref_dev) + " > ref_tol";
+            c->gate = "oracle";
+            c->why = "reference term " + std::to_string(term) + ": deviation " + fmt(c->ref_dev[k]) + " > ref_tol";
             return;
         }
     }
@@ -527,19 +567,23 @@ void Tuner::start_unit(int unit, UnitSearch* u) {
         for (float x : def_out_[unit][k]) peak = std::max(peak, (double)std::fabs(x));
         noise_[unit][k] = std::max(max_abs_diff(def_out_[unit][k], pert.data(), pert.size()), 1e-6 * peak);
         d.t[k] = def_t_[unit][k];
+        d.dev[k] = 0.0;                         // the default is the alpha gate's reference
     }
-    if (d.verdict.empty() && req_.ref_cache && (unit ? req_.ref_q_verify && req_.ref_out_verify : req_.ref_q && req_.ref_out)) {
-        const float* ref = unit ? req_.ref_out_verify : req_.ref_out;
-        const size_t n = (size_t)(unit ? w_ : 1) * hq_ * d_;
-        ref_host_[unit].assign(ref, ref + n);
+    for (int k = 0; k < 2 && d.verdict.empty(); ++k) {
+        const int term = 2 * unit + k;
+        if (!has_ref(term)) continue;
         std::vector<float> o;
-        if (ref_output(&dflt, unit == 1, &o) != Q8K4V_OK) { d.verdict = "invalid"; d.why = q8k4v_last_error(); }
-        else d.ref_dev = max_abs_diff(o, ref_host_[unit].data(), n);
+        if (ref_output(&dflt, term, &o) != Q8K4V_OK) { d.verdict = "invalid"; d.why = q8k4v_last_error(); break; }
+        d.ref_dev[k] = ref_deviation(term, o);
+        if (!(d.ref_dev[k] <= req_.ref_tol)) {
+            d.verdict = "rejected";
+            d.gate = "oracle";
+            d.why = "reference term " + std::to_string(term) + ": deviation " + fmt(d.ref_dev[k]) + " > ref_tol";
+        }
     }
     if (d.verdict.empty()) {
         d.cost = 2.0;
-        d.verdict = (d.ref_dev < 0 || d.ref_dev <= req_.ref_tol) ? "admitted" : "rejected";
-        if (d.verdict == "rejected") d.why = "reference deviation " + fmt(d.ref_dev) + " > ref_tol";
+        d.verdict = "admitted";
     }
     d.seq = seq_++;
     u->cands.push_back(d);
@@ -548,14 +592,11 @@ void Tuner::start_unit(int unit, UnitSearch* u) {
     u->effort_ms = u->price_ms;
     u->active = d.verdict == "admitted";
     if (!u->active) return;
-    // structural variants: which kernel runs the unit (each with its own
-    // launch-shape defaults)
+    // structural variant: the other kernel, where it runs the unit (the
+    // row-block kernel takes any row count; the replicated-row kernel only
+    // 1, 2, 4, 8 or 16 rows), with its own launch-shape defaults
     std::vector<int> variants;
-    if (paged16) {
-        if (rows == 4 || rows == 8) variants.push_back(2);
-        if (rows <= 8) variants.push_back(1);
-    }
-    variants.push_back(3);
+    if (paged16) variants.push_back(5);
     for (int v : variants) {
         Cand c;
         c.cfg = dflt;
@@ -580,30 +621,21 @@ void Tuner::refine_queue(int unit, UnitSearch* u) {
         u->queue.push_back(x);
         ++u->generated;
     };
-    for (int fused : {0, 1}) {
-        if (base_paged) {
-            for (int stages : {3, 2})
-                for (int waves : {4, 8, 2})
-                    for (int wgs : {2, 1, 3, 4, 6}) {
-                        if (waves == 8 && wgs > 1) continue;   // one 8-wave workgroup fills a CU's LDS
-                        q8k4v_config c = base;
-                        c.waves_per_wg = waves;
-                        c.wgs_per_cu = wgs;
-                        c.stages = stages;
-                        c.fused_combine = fused;
-                        push(c);
-                    }
-        } else {
-            for (int waves : {2, 4, 1})
-                for (int wgs : {5, 4, 6, 3, 8, 2, 12, 1}) {
+    // launch shapes both kernels accept: 2, 4 or 8 waves, 2 or 3 stages; one
+    // 8-wave workgroup fills a CU's LDS, so 8 waves take one or two per CU
+    for (int fused : {0, 1})
+        for (int stages : {2, 3})
+            for (int waves : {4, 8, 2})
+                for (int wgs : {1, 2, 3, 4, 6}) {
+                    if (waves == 8 && wgs > 2) continue;
+                    if (!base_paged && waves == 2 && wgs > 4) continue;
                     q8k4v_config c = base;
                     c.waves_per_wg = waves;
                     c.wgs_per_cu = wgs;
+                    c.stages = stages;
                     c.fused_combine = fused;
                     push(c);
                 }
-        }
-    }
 }
 
 // ---- records ----------------------------------------------------------------
@@ -848,12 +880,17 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     std::string cand_lists;
     for (int unit = 0; unit < 2; ++unit) {
         if (unit) j += ",";
-        int n_adm = 0, n_rej = 0, n_unk = 0, n_inv = 0;
+        int n_adm = 0, n_rej = 0, n_unk = 0, n_inv = 0, n_alpha = 0, n_oracle = 0;
+        std::vector<std::string> invalid_why;
         for (const auto& c : cands[unit]) {
             n_adm += c.verdict == "admitted";
             n_rej += c.verdict == "rejected";
             n_unk += c.verdict == "unknown";
             n_inv += c.verdict == "invalid";
+            n_alpha += c.gate == "alpha";
+            n_oracle += c.gate == "oracle";
+            if (c.verdict == "invalid" && std::find(invalid_why.begin(), invalid_why.end(), c.why) == invalid_why.end())
+                invalid_why.push_back(c.why);
         }
         j += "{\"unit\":\"" + std::string(unit ? "verify" : "decode") + "\"";
         j += ",\"rows_per_kv_head\":" + std::to_string((unit ? w_ : 1) * g_);
@@ -863,6 +900,12 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
         j += ",\"searched\":" + std::to_string(cands[unit].size());
         j += ",\"admitted\":" + std::to_string(n_adm) + ",\"rejected\":" + std::to_string(n_rej) +
              ",\"unknown\":" + std::to_string(n_unk) + ",\"invalid\":" + std::to_string(n_inv);
+        j += ",\"rejected_by\":{\"alpha\":" + std::to_string(n_alpha) + ",\"oracle\":" + std::to_string(n_oracle) + "}";
+        j += ",\"oracle_gate\":[" + std::string(has_ref(2 * unit) ? "true" : "false") + "," +
+             std::string(has_ref(2 * unit + 1) ? "true" : "false") + "]";
+        j += ",\"invalid_why\":[";
+        for (size_t i = 0; i < invalid_why.size(); ++i) j += (i ? ",\"" : "\"") + json_text(invalid_why[i]) + "\"";
+        j += "]";
         j += ",\"qualified\":" + std::string(qual[unit] ? "true" : "false");
         j += ",\"chosen\":" + cfg_json(out_table[unit]);
         double best_cost = 2.0, best_t0 = def_t_[unit][0], best_t1 = def_t_[unit][1];
@@ -879,13 +922,9 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
                           fmt(c.dev[1]) + "],\"cost\":" + fmt(c.cost) + ",\"seq\":" + std::to_string(c.seq) +
                           ",\"vt\":[" + (c.vt[0] < 0 ? std::string("null") : fmt(c.vt[0])) + "," +
                           (c.vt[1] < 0 ? std::string("null") : fmt(c.vt[1])) + "]";
-            if (c.ref_dev >= 0) cand_lists += ",\"ref_dev\":" + fmt(c.ref_dev);
-            if (!c.why.empty()) {
-                std::string w = c.why;
-                for (auto& ch : w)
-                    if (ch == '"' || ch == '\\' || (unsigned char)ch < 32) ch = ' ';
-                cand_lists += ",\"why\":\"" + w + "\"";
-            }
+            cand_lists += ",\"ref_dev\":[" + fmt(c.ref_dev[0]) + "," + fmt(c.ref_dev[1]) + "]";
+            if (!c.gate.empty()) cand_lists += ",\"gate\":\"" + c.gate + "\"";
+            if (!c.why.empty()) cand_lists += ",\"why\":\"" + json_text(c.why) + "\"";
             cand_lists += "}";
         }
         cand_lists += "]";
@@ -922,9 +961,14 @@ extern "C" int32_t tune_select(const q8k4v_tune_request* req, q8k4v_config* out_
     if (req->n_draft < 1 || req->n_draft > Q8K4V_MAX_DRAFT) return fail(Q8K4V_EINVAL, "tune_select: n_draft must be in 1..16");
     if (req->ctx_small < 1 || req->ctx_large < req->ctx_small)
         return fail(Q8K4V_EINVAL, "tune_select: need 1 <= ctx_small <= ctx_large");
-    if (req->ref_cache && (req->ref_len < req->n_draft || !req->ref_page_table || req->ref_max_pages < 1 ||
-                           (int64_t)req->ref_max_pages * Q8K4V_PAGE_SIZE < req->ref_len))
-        return fail(Q8K4V_EINVAL, "tune_select: inconsistent reference inputs");
+    for (int k = 0; k < 4; ++k) {
+        const q8k4v_tune_ref& r = req->ref[k];
+        if (!r.cache) continue;
+        const int n = k >= 2 ? req->n_draft : 1;
+        if (!r.q || !r.page_table || !r.out || r.len < n || r.max_pages < 1 ||
+            (int64_t)r.max_pages * Q8K4V_PAGE_SIZE < r.len)
+            return fail(Q8K4V_EINVAL, "tune_select: inconsistent reference inputs for term " + std::to_string(k));
+    }
     const int64_t budget = std::max<int64_t>(0, std::min<int64_t>(req->budget_ms, kMaxBudgetMs));
     Tuner t(*req, t0 + std::chrono::milliseconds(budget));
     std::string report;

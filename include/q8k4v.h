@@ -67,6 +67,11 @@ extern "C" {
 #define Q8K4V_MAX_DRAFT 16
 #define Q8K4V_MAX_CHUNK 1024     /* new tokens per sequence in one prefill call */
 
+/* Every workspace starts with a header of this many bytes that holds the
+ * arrival counters of the in-launch split merge (fused_combine); split
+ * records of every plan and entry point lie behind it. */
+#define Q8K4V_WS_HEADER_BYTES 65536
+
 #define Q8K4V_CODEC_SYMMETRIC 0   /* the codec above                            */
 #define Q8K4V_CODEC_AFFINE    1   /* the affine variant below                   */
 
@@ -81,8 +86,7 @@ extern "C" {
  *   values (per token, kv head and 32 dims); s == 0 gives code and z 0.
  *   k_codes hold code XOR 0x80 (code - 128 as int8), k_zeros z XOR 0x80;
  *   value nibbles hold the unsigned codes, v_zeros one byte (0..15) per
- *   (token, group).  Attention on an affine cache runs on variants 4 and 5
- *   (and the automatic choice); variants 1-3 return EUNSUPPORTED. */
+ *   (token, group).  Every attention entry point takes either codec. */
 typedef struct q8k4v_cache {
     int32_t   num_pages;     /* P: physical pages in each pool                   */
     int32_t   num_kv_heads;  /* H                                                */
@@ -103,24 +107,24 @@ typedef struct q8k4v_config {
     int32_t wgs_per_cu;      /* split-K: target workgroups per compute unit; the split
                                 length follows from it and the launch shape           */
     int32_t split_pages;     /* if > 0: pages per workgroup split (overrides wgs_per_cu) */
-    int32_t tile_pages;      /* pages staged in LDS per wave per step: 1, 2 or 4 (the
-                                MFMA variants fix it: 4 for 2, 2 for 3 and 4)          */
-    int32_t waves_per_wg;    /* 1, 2 or 4 waves per workgroup (variants 4 and 5: 2, 4
-                                or 8). Default 4, or 8 for variant 5 above 16 rows
-                                per kv head                                           */
-    int32_t fused_combine;   /* 1: the last workgroup of a (sequence, kv head) merges
-                                the splits (needs a zeroed workspace counter area);
-                                0: a separate combine kernel                           */
+    int32_t tile_pages;      /* pages staged in LDS per wave per step: both kernels
+                                stage 2-page tiles (0 or 2; anything else EINVAL)     */
+    int32_t waves_per_wg;    /* 2, 4 or 8 waves per workgroup. Default 4, or 8 for
+                                variant 5 above 16 rows per kv head                   */
+    int32_t fused_combine;   /* 1: the last workgroup of a (sequence, kv head, row
+                                chunk) merges the splits in the same launch (its
+                                arrival counters live in the workspace header; a
+                                launch with more than Q8K4V_WS_HEADER_BYTES / 4 such
+                                items uses the separate kernel); 0: a separate combine
+                                kernel                                                  */
     int32_t qualified;       /* out of tune_select: 1 measured and admitted, 0 default */
-    int32_t variant;         /* 0 auto: 4 for 1, 2, 4, 8 or 16 query rows per kv head,
-                                else 5; 1 vector ALUs (1, 2, 4 or 8 rows); 2 4x4x4 block
-                                MFMA (4 or 8 rows); 3 16x16 MFMA, 16 or 32 rows per
-                                workgroup (any row count); 4 16x16 MFMA with the rows
-                                replicated across the columns (1, 2, 4, 8 or 16 rows);
-                                5 16x16 MFMA row blocks with the tile ring, 16 or
-                                32 rows per workgroup (any row count)                  */
-    int32_t stages;          /* variants 4, 5: tile buffers per wave in the HBM->LDS ring,
-                                2 or 3 (prefetch depth stages - 1); 0 default        */
+    int32_t variant;         /* kernel: 0 automatic (4 for 1, 2, 4, 8 or 16 query rows
+                                per kv head, else 5); 4 16x16 MFMA with the rows
+                                replicated across the MFMA columns (1, 2, 4, 8 or 16
+                                rows); 5 16x16 MFMA row blocks, 16 or 32 rows per
+                                workgroup (any row count).  Other values EINVAL      */
+    int32_t stages;          /* tile buffers per wave in the HBM->LDS ring, 2 or 3
+                                (prefetch depth stages - 1); 0 default               */
 } q8k4v_config;
 
 /* Last error message of the calling thread ("" if none). */
@@ -159,12 +163,16 @@ int32_t kv_quant_append(const q8k4v_cache *cache, const void *k_new, const void 
  * Workspace (bytes) that attn_decode_q8k4v / attn_verify_q8k4v need for the
  * given launch shape and configuration (cfg may be NULL for the defaults);
  * n_draft = 0 for decode, the draft count for verify, the chunk length for
- * prefill.  Returns 0 on invalid shapes.  The workspace holds
- * the split-K partials and, with fused_combine, a counter area that must be
- * zero when first used; the library leaves the counters at zero after each
- * completed call, so zero the workspace once after allocating it.  The
- * partials need no initial value: records of splits past a sequence's last
- * page are masked by the merge, never read as values.
+ * prefill.  Returns 0 on invalid shapes, and 0 when the launch runs as one
+ * split per (sequence, kv head) (it then writes the output directly and
+ * needs no workspace).  Otherwise the workspace is the header of
+ * Q8K4V_WS_HEADER_BYTES followed by the split-K partials.  The header holds
+ * the in-launch merge's arrival counters: it must be zero before its first
+ * use; every completed call of every entry point leaves it zero, and no
+ * entry point writes split records into it, so a workspace zeroed once (at
+ * least its header) serves any sequence of calls, plans, shapes and entry
+ * points.  The partials need no initial value: records of splits past a
+ * sequence's last page are masked by the merge, never read as values.
  */
 size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t max_seq_len, int32_t n_draft,
@@ -235,9 +243,10 @@ int32_t attn_decode_prefix_q8k4v(const q8k4v_cache *cache, const void *q, int32_
                                  const q8k4v_config *cfg, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
-/* Workspace (bytes) of attn_decode_prefix_q8k4v: both passes' split
- * partials (no counters, nothing to zero), enough for either codec.
- * Returns 0 on invalid shapes. */
+/* Workspace (bytes) of attn_decode_prefix_q8k4v: the header of
+ * Q8K4V_WS_HEADER_BYTES (the cascade keeps no counters but writes no records
+ * into it, so one workspace serves every entry point) and both passes' split
+ * partials, enough for either codec.  Returns 0 on invalid shapes. */
 size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t max_seq_len, int32_t n_prefix_pages,
                                     const q8k4v_config *cfg);
@@ -250,10 +259,11 @@ size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t
  * The drafts' keys/values must already be appended: seq_lens[b] counts them,
  * and draft j (0-based) of sequence b attends positions 0 .. seq_lens[b] -
  * n_draft + j.  Rows (draft, q head) of one kv head form a
- * (n_draft * group) x D query block.  With 1, 2, 4 or 8 rows it runs on the
- * kernels of attn_decode_q8k4v; any other row count is a dense contraction
- * on 16x16 MFMA tiles: q.K on int8 MFMA (raw key codes against the query as a
- * 15-bit fixed-point number split into two int8 halves, int32 accumulation),
+ * (n_draft * group) x D query block.  With 1, 2, 4, 8 or 16 rows it runs on
+ * the decode kernel (rows replicated across the MFMA columns); any other row
+ * count on 16x16 MFMA row blocks: q.K on int8 MFMA (raw key codes against
+ * the query as a 23-bit fixed-point number per row, three int8 digits,
+ * int32 accumulation),
  * P.V on fp16 MFMA (exact value codes against each probability times the
  * token's value scale for that 32-dim group, rounded to fp16; fp32
  * accumulation).
@@ -319,6 +329,39 @@ int32_t attn_prefill_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dt
                            hipStream_t stream);
 
 /*
+ * q8k4v_hbm_probe -- streaming reference of the decode kernel's roofline
+ * (the survey's memory probe; measurement only, outside the hot path).
+ * Reads exactly the bytes attn_decode_q8k4v reads over the same arguments --
+ * every (page, kv head) block of key codes, value codes, key scales and
+ * value scales of each sequence's pages through page_table, with the decode
+ * plan's split of pages over workgroups and its XCD-aware mapping, in 2-page
+ * tiles copied HBM -> LDS -- and computes nothing.  Its time is what the
+ * memory system gives that access pattern; blog.123qwe.co.kr/?p=3927,
+ * section 5, gives the reason decode is judged by it (decode is bound by
+ * memory traffic).
+ *   cache, n_seqs, seq_lens, max_seq_len, page_table, max_pages: as
+ *                 attn_decode_q8k4v (symmetric codec only)
+ *   waves_per_wg, stages: launch shape, (4, 2..4) or (8, 2..3); stages - 1
+ *                 tiles per wave in flight
+ * Errors: EINVAL (shape, codec, launch shape), EHIP.  Writes nothing to
+ * device memory.
+ */
+int32_t q8k4v_hbm_probe(const q8k4v_cache *cache, int32_t n_seqs, const int32_t *seq_lens,
+                        int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
+                        int32_t waves_per_wg, int32_t stages, hipStream_t stream);
+
+/*
+ * q8k4v_stream_probe -- the sequential reference: streams `bytes` of the
+ * contiguous device buffer `buf` into LDS, one chunk per compute unit, in
+ * 1 KiB wave copies with (stages - 1) x 4 KiB per wave in flight.
+ *   buf       device, 16-byte aligned; bytes >= 1024 and a multiple of 16
+ *   waves_per_wg 4 or 8; stages 2..4
+ * Errors: EINVAL, EHIP.  Writes nothing to device memory.
+ */
+int32_t q8k4v_stream_probe(const void *buf, size_t bytes, int32_t waves_per_wg, int32_t stages,
+                           hipStream_t stream);
+
+/*
  * tune_select -- on-device search of the attention launch configuration
  * (blog.123qwe.co.kr/?p=3927, section 3: first-load tuner).
  *
@@ -337,16 +380,22 @@ int32_t attn_prefill_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dt
  * (section 4 of the same page, alpha = 8): on every checked output the
  * candidate's deviation from the default configuration's output must not
  * exceed alpha times the storage-resolution noise, i.e. the change of the
- * default output when every stored code is moved by one step; and, when the
- * caller supplies reference outputs, the deviation from them must not
- * exceed ref_tol.  Search order (section 3): after both defaults, each next
- * candidate comes from the unit with the earliest virtual completion time
- * (effort + price) / (share x opportunity) -- wall time spent on the unit,
- * wall time of its last measurement, its part of the default service time,
- * the fraction of its generated candidates still unmeasured; within a unit,
- * structurally different kernels before launch-shape refinement.  The JSON
- * report lists every candidate with its verdict, measurement order ("seq")
- * and both units' virtual times when it was picked ("vt").
+ * default output when every stored code is moved by one step; and, on each
+ * of the four terms for which the caller supplies a reference output (the
+ * oracle gate: "keep only configurations whose output matches the oracle"),
+ * the sigma-normalised deviation from it must not exceed ref_tol.  Search
+ * order (section 3): after both defaults, each next candidate comes from the
+ * unit with the earliest virtual completion time (effort + price) / (share x
+ * opportunity) -- wall time spent on the unit, wall time of its last
+ * measurement, its part of the default service time, the fraction of its
+ * generated candidates still unmeasured; within a unit, the other kernel
+ * before launch-shape refinement, and only configurations the library
+ * accepts.  The JSON report lists every candidate with its verdict, the gate
+ * that rejected it ("alpha" or "oracle") and why, its deviations (null where
+ * not measured: unknown, never 0), its measurement order ("seq") and both
+ * units' virtual times when it was picked ("vt"); each unit's summary counts
+ * the rejections per gate and lists the distinct reasons of invalid
+ * candidates.
  *
  *   req         host, see q8k4v_tune_request
  *   out_table   host [2]: [0] decode, [1] verify; `qualified` = 1 if a
@@ -356,6 +405,19 @@ int32_t attn_prefill_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dt
  * unqualified); ENOMEM if memory admission refuses even the defaults;
  * EINVAL on bad shapes; EHIP.
  */
+/* One reference term of the tuner's oracle gate: a sequence in the caller's
+ * cache with its expected attention output (e.g. from a CPU oracle). */
+typedef struct q8k4v_tune_ref {
+    const q8k4v_cache *cache;          /* device pools; NULL: no reference for this term  */
+    const void *q;                     /* device bf16 [n][num_q_heads][D]; n = 1 for the
+                                          decode terms, n_draft for the verify terms      */
+    const int32_t *page_table;         /* device int32 [max_pages]: the sequence's pages  */
+    int32_t len, max_pages;            /* tokens attended (the drafts included for verify) */
+    const float *out;                  /* host float32 [n][num_q_heads][D]                */
+    const float *sigma;                /* host float32 [num_q_heads][D] or NULL (1): the
+                                          deviation is |out - ref| / sigma per element    */
+} q8k4v_tune_ref;
+
 typedef struct q8k4v_tune_request {
     int32_t num_q_heads, num_kv_heads, head_dim, n_draft;
     int32_t ctx_small, ctx_large;      /* e.g. 4096 and 65536 */
@@ -367,16 +429,14 @@ typedef struct q8k4v_tune_request {
                                           (n_draft, num_q_heads, num_kv_heads, head_dim);
                                           the decode unit is stored under n_draft 1 */
     int32_t max_candidates;            /* 0: no limit */
-    /* optional gate against caller references on caller inputs (may be NULL):
-       ref_cache + ref_q/ref_out for decode at ref_len (one sequence) */
-    const q8k4v_cache *ref_cache;
-    const void *ref_q;                 /* device, bf16 [num_q_heads][D] (decode)            */
-    const void *ref_q_verify;          /* device, bf16 [n_draft][num_q_heads][D] (verify)    */
-    const int32_t *ref_page_table;     /* device int32 [ref_max_pages]                      */
-    int32_t ref_len, ref_max_pages;
-    const float *ref_out;              /* host float32 [num_q_heads][D]                     */
-    const float *ref_out_verify;       /* host float32 [n_draft][num_q_heads][D]            */
-    float ref_tol;                     /* absolute tolerance against the references         */
+    /* Oracle gate (optional per term; the tuner never computes references
+       itself): ref[k] for term k = decode@ctx_small, decode@ctx_large,
+       verify@ctx_small, verify@ctx_large.  A term with ref[k].cache != NULL
+       runs every candidate on the caller's inputs and admits it only if
+       max |out - ref[k].out| / ref[k].sigma <= ref_tol.  The default must pass
+       too, else the unit keeps unqualified defaults. */
+    q8k4v_tune_ref ref[4];
+    float ref_tol;                     /* tolerance on the normalised deviation            */
     float softmax_scale;               /* 0: 1/sqrt(D)                                      */
     /* optional text file of stored choices (may be NULL): a call whose device
        identity (architecture, device name and CU count, HIP runtime and driver

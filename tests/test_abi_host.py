@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("kv_quant_append", "attn_decode_q8k4v", "attn_verify_q8k4v", "tune_select",
-              "attn_decode_prefix_q8k4v", "q8k4v_prefix_workspace_bytes", "attn_prefill_q8k4v"):
+              "attn_decode_prefix_q8k4v", "q8k4v_prefix_workspace_bytes", "attn_prefill_q8k4v",
+              "q8k4v_hbm_probe", "q8k4v_stream_probe"):
         assert n in names
 
 
@@ -93,21 +94,48 @@ def test_attention_rejects_bad_arguments(lib):
     assert rc == -3 and b"workspace" in lib.q8k4v_last_error()
 
 
+WS_HEADER = 65536      # Q8K4V_WS_HEADER_BYTES
+
+
 def test_workspace_size_follows_the_plan(lib):
     small = q8.workspace_bytes(1, 32, 8, 128, 64)
     big = q8.workspace_bytes(1, 32, 8, 128, 65536)
     assert big > 0 and big >= small
-    cfg = q8.make_config(split_pages=4096, variant=2)
-    assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, cfg) == 0     # one split: direct write
+    cfg = q8.make_config(split_pages=32, variant=5)
+    assert q8.workspace_bytes(1, 32, 8, 128, 512, 0, cfg) == 0       # one split: direct write, no workspace
     # variant 4 keeps at most 64 pages per wave: 4096 pages need splits
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(split_pages=4096, variant=4)) > 0
     assert q8.workspace_bytes(1, 32, 8, 128, 65536, 0, q8.make_config(waves_per_wg=3)) == 0  # invalid config
-    assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(variant=2)) == 0  # 1 row: no block MFMA
+    for v in (1, 2, 3, 6):                                             # only 0 (automatic), 4 and 5
+        assert q8.workspace_bytes(1, 32, 8, 128, 4096, 0, q8.make_config(variant=v)) == 0
+    assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(tile_pages=4)) == 0
+
+
+def test_workspace_header_is_shared_by_every_plan(lib):
+    """Every plan that writes split records puts them behind one fixed
+    header, and the in-launch merge keeps its counters inside that header:
+    the fused and the separate merge need the same bytes, and no plan's
+    records (decode, verify, prefill, cascade, at any length) can reach the
+    counters of another.  (With the counters behind each plan's own records,
+    a verify launch's records at 64K covered the 4K decode's counters.)"""
+    shapes = [(1, 32, 8, 128, 4096, 0), (1, 32, 8, 128, 65536, 0), (1, 32, 8, 128, 65544, 8),
+              (1, 32, 8, 128, 4104, 8), (1, 32, 8, 128, 65536 + 512, 512), (16, 32, 4, 128, 65536, 0)]
+    for sh in shapes:
+        plain = q8.workspace_bytes(*sh, q8.make_config(fused_combine=0))
+        fused = q8.workspace_bytes(*sh, q8.make_config(fused_combine=1))
+        assert plain == fused and plain > WS_HEADER, (sh, plain, fused)
+        assert (plain - WS_HEADER) % 256 == 0
+        # records: n_seqs x H x splits x rows x (D + 4) floats behind the header
+        n, hq, h, d, _, nd = sh
+        rows = (hq // h) * max(1, nd)
+        assert (plain - WS_HEADER) >= n * h * 8 * rows * (d + 4) * 4
+    pre = q8.prefix_workspace_bytes(16, 32, 4, 128, 65536, 2048)
+    assert pre > WS_HEADER
 
 
 def test_affine_cache_validation(lib):
-    """An affine cache needs its zero-point pools; its attention runs on
-    variants 4 and 5 only; an unknown codec is refused (all before a launch)."""
+    """An affine cache needs its zero-point pools; an unknown codec and an
+    unknown kernel variant are refused (all before a launch)."""
     d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, q8.CODEC_AFFINE, None, None)
     args = (1, 1, 1, 1, 32, 1, 64, 1, 4, 0.1)
     assert lib.attn_decode_q8k4v(C.byref(d), *args, None, None, 0, None) == -1
@@ -116,10 +144,10 @@ def test_affine_cache_validation(lib):
     d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, 7, 1, 1)
     assert lib.attn_decode_q8k4v(C.byref(d), *args, None, None, 0, None) == -1
     d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, q8.CODEC_AFFINE, 1, 1)
-    for v in (1, 2, 3):
+    for v in (1, 2, 3, 6):
         cfg = q8.make_config(variant=v)
-        assert lib.attn_decode_q8k4v(C.byref(d), *args, C.byref(cfg), None, 0, None) == -2, v
-        assert b"affine" in lib.q8k4v_last_error()
+        assert lib.attn_decode_q8k4v(C.byref(d), *args, C.byref(cfg), None, 0, None) == -1, v
+        assert b"variant" in lib.q8k4v_last_error()
 
 
 def test_prefix_cascade_validation_and_workspace(lib):
@@ -165,6 +193,19 @@ def test_tuner_rejects_bad_requests(lib):
     assert tune(ctx_small=0) == -1
     assert tune(ctx_small=8192, ctx_large=4096) == -1
     assert lib.tune_select(None, None, None, 0) == -1
+    # a reference term with a cache but an inconsistent length / table
+    r = q8.TuneRequest()
+    for k, v in dict(num_q_heads=32, num_kv_heads=8, head_dim=128, n_draft=8, ctx_small=4096,
+                     ctx_large=65536, budget_ms=1000).items():
+        setattr(r, k, v)
+    d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1)
+    r.ref[2].cache = C.pointer(d)
+    r.ref[2].q, r.ref[2].page_table, r.ref[2].out = 1, 1, 1
+    r.ref[2].len, r.ref[2].max_pages = 4, 64          # verify term shorter than its 8 drafts
+    table = (q8.Config * 2)()
+    assert lib.tune_select(C.byref(r), table, None, 0) == -1 and b"term 2" in lib.q8k4v_last_error()
+    r.ref[2].len, r.ref[2].max_pages = 4104, 64       # 64 pages cannot hold 4104 tokens
+    assert lib.tune_select(C.byref(r), table, None, 0) == -1
 
 
 def test_binding_rejects_host_tensors():
@@ -189,10 +230,23 @@ def test_long_context_splits_are_even(lib):
 
     def splits(ctx, n_new=0):
         rows = 4 * max(1, n_new)
-        return q8.workspace_bytes(1, 32, 8, 128, ctx, n_new) / (8 * rows * rec)
+        return (q8.workspace_bytes(1, 32, 8, 128, ctx, n_new) - WS_HEADER) / (8 * rows * rec)
 
     assert splits(65536) == 32 and splits(131072) == 32       # under the cap: one workgroup per CU
     for ctx in (163840, 200000, 262144):
         s = splits(ctx)
         assert s == 64, (ctx, s)                             # two per CU, 8 per XCD
     assert splits(65536 + 512, 512) == 16                    # 9 capped splits, padded to 16
+
+
+def test_probes_reject_bad_arguments(lib):
+    """The streaming probes validate before any launch."""
+    d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1)
+    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 4, 5, None) == -1       # stages
+    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 2, 2, None) == -1       # waves
+    da = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, q8.CODEC_AFFINE, 1, 1)
+    assert lib.q8k4v_hbm_probe(C.byref(da), 1, 1, 1024, 1, 64, 4, 3, None) == -1      # symmetric only
+    assert lib.q8k4v_stream_probe(None, 4096, 4, 3, None) == -1
+    assert lib.q8k4v_stream_probe(16, 1000, 4, 3, None) == -1                         # too short
+    assert lib.q8k4v_stream_probe(16, 4100, 4, 3, None) == -1                         # not a multiple of 16
+    assert lib.q8k4v_stream_probe(16, 4096, 4, 5, None) == -1

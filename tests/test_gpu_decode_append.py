@@ -52,7 +52,7 @@ def _run(w, cfg, codec="symmetric"):
 
 
 CFGS = [None, dict(fused_combine=1), dict(split_pages=4096), dict(variant=4, stages=3), dict(variant=4, waves_per_wg=8),
-        dict(variant=3), dict(variant=1)]
+        dict(variant=5), dict(variant=5, waves_per_wg=8, fused_combine=1)]
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=str)

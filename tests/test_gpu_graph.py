@@ -35,7 +35,7 @@ def _replays_match(fn, out, n=4):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg", [None, dict(fused_combine=1), dict(variant=3)], ids=str)
+@pytest.mark.parametrize("cfg", [None, dict(fused_combine=1), dict(variant=5)], ids=str)
 def test_decode_graph_replays(cfg):
     import decode_attention_quantized_kv_amd as q8
     from tests.gpu_util import to_dev, upload_cache

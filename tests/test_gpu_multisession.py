@@ -19,8 +19,8 @@ def _check(w, got, want, label):
     assert err <= ATOL_SIGMA, (label, err)
 
 
-@pytest.mark.parametrize("cfg", [None, dict(variant=3), dict(variant=1), dict(variant=2),
-                                 dict(variant=4, stages=2, waves_per_wg=2)], ids=str)
+@pytest.mark.parametrize("cfg", [None, dict(variant=5), dict(variant=5, waves_per_wg=2, stages=3),
+                                 dict(fused_combine=1), dict(variant=4, stages=2, waves_per_wg=2)], ids=str)
 def test_ragged_sessions_with_shared_prefix(cfg):
     import decode_attention_quantized_kv_amd as q8
     from tests.gpu_util import run_attention, upload_cache

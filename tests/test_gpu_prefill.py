@@ -46,7 +46,7 @@ def test_chunk_parity(hq, hkv, D, dt, n_new, lens):
                         seq_lens=[L + n_new for L in lens] if lens[0] != n_new else lens, n_draft=n_new,
                         outliers=True)
     cache, oc = upload_cache(w), oracle_cache(w)
-    for cfg in (None, dict(variant=5, waves_per_wg=4), dict(variant=3)):
+    for cfg in (None, dict(variant=5, waves_per_wg=4), dict(variant=5, waves_per_wg=2, stages=3)):
         _check(w, cache, oc, cfg, f"Hq {hq} Hkv {hkv} D {D} n_new {n_new}")
 
 

@@ -23,7 +23,8 @@ def _check(w, got, want, label):
 
 
 @pytest.mark.parametrize("cfg", [None, dict(variant=4, stages=2, waves_per_wg=2), dict(variant=4, stages=3),
-                                 dict(variant=3), dict(variant=2), dict(variant=1), dict(wgs_per_cu=3)], ids=str)
+                                 dict(variant=5), dict(variant=5, waves_per_wg=8), dict(fused_combine=1),
+                                 dict(wgs_per_cu=3)], ids=str)
 def test_ragged_sessions_every_suffix_kernel(cfg):
     import decode_attention_quantized_kv_amd as q8
     from tests.gpu_util import run_prefix, upload_cache

@@ -13,9 +13,8 @@ from oracle import attention
 
 pytestmark = pytest.mark.gpu
 
-DECODE_CFGS = [None, dict(variant=1), dict(variant=2), dict(variant=3), dict(variant=4, waves_per_wg=8),
-               dict(fused_combine=1)]
-VERIFY_CFGS = [None, dict(variant=3), dict(variant=5, waves_per_wg=4), dict(fused_combine=1)]
+DECODE_CFGS = [None, dict(variant=5), dict(variant=4, waves_per_wg=8), dict(fused_combine=1)]
+VERIFY_CFGS = [None, dict(variant=5, waves_per_wg=4), dict(fused_combine=1)]
 
 
 def _run(w, cache, scale, cfg):

@@ -51,10 +51,22 @@ def test_tuner_budget_rotation_and_admitted_parity():
         assert cands[0]["stage"] == "default" and cands[0]["verdict"] == "admitted"
         assert unit["qualified"] and cfg.qualified == 1
         assert unit["chosen_cost"] <= 2.0 + 1e-9
+        assert unit["invalid"] == 0, unit["invalid_why"]   # no candidate the library refuses
         for c in cands:
             if c["verdict"] == "admitted":
                 assert c["us"][0] > 0 and c["us"][1] > 0
                 assert max(c["dev"]) <= rep["alpha"] * max(unit["noise"])
+            if c["verdict"] == "rejected":
+                assert c["gate"] == "alpha" and c["why"]
+            # a deviation is null only when it was not measured (deadline or
+            # an earlier rejection), never reported as 0
+            if c["verdict"] == "admitted":
+                assert all(d is not None for d in c["dev"])
+        # in-launch-merge candidates write their outputs on both shapes (one
+        # workspace serves every candidate of both units)
+        fused = [c for c in cands if c["cfg"]["fused_combine"] == 1 and c["verdict"] != "unknown"]
+        assert fused and all(c["dev"][0] is not None and c["verdict"] == "admitted" for c in fused), \
+            [(c["cfg"], c["verdict"], c.get("why")) for c in fused if c["verdict"] != "admitted"]
         chosen = unit["chosen"]
         assert {k: getattr(cfg, k) for k in chosen} == chosen
         # the noise floor is real: moving every code by one step moves the output
@@ -81,37 +93,42 @@ def test_tuner_memory_admission_refuses():
     assert e.value.code == -5
 
 
-def _reference(hq, hkv, D, W, L, seed):
-    """Caller references: the oracle's verify output on a small cache and the
-    decode output of the last draft's query at the full length."""
+def _references(hq, hkv, D, W, L_small, L_large, seed):
+    """Oracle references for the tuner's four terms on caller inputs: decode
+    and verify at a small and a large context (two sequences with W drafts
+    appended; decode attends the context before the drafts)."""
+    from oracle import attention
     from tests.gpu_util import to_dev, upload_cache
-    w = workloads.build("tref", seed=seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, dtype="bf16",
-                        seq_lens=[L], n_draft=W, outliers=False)
-    cache = upload_cache(w)
-    want = oracle_out(w)                     # [1][W][Hq][D]
-    return w, {
-        "cache": cache,
-        "q": to_dev(np.ascontiguousarray(w.q[0, W - 1]), "bf16"),
-        "q_verify": to_dev(np.ascontiguousarray(w.q[0]), "bf16"),
-        "page_table": to_dev(np.ascontiguousarray(w.page_table[0])),
-        "length": L,
-        "out": want[0, W - 1].astype(np.float32),
-        "out_verify": want[0].astype(np.float32),
-        "tol": ATOL_SIGMA,
-    }
+    from tests.util import oracle_cache, sigma_q_heads
+    refs = {}
+    for size, L in (("small", L_small), ("large", L_large)):
+        w = workloads.build("tref_" + size, seed=seed + L, num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
+                            dtype="bf16", seq_lens=[L + W], n_draft=W, outliers=True)
+        cache, oc = upload_cache(w), oracle_cache(w)
+        ver = oracle_out(w, oc)                                        # [1][W][Hq][D]
+        qd = np.ascontiguousarray(w.q[:, 0])                           # [1][Hq][D]
+        dec = attention.decode(oc, qd, w.dtype, w.page_table, np.array([L], np.int32), w.softmax_scale)
+        pt = to_dev(np.ascontiguousarray(w.page_table[0]))
+        sig = sigma_q_heads(w)
+        refs["decode_" + size] = {"cache": cache, "q": to_dev(qd[0], "bf16"), "page_table": pt, "length": L,
+                                  "out": dec[0].astype(np.float32), "sigma": sig}
+        refs["verify_" + size] = {"cache": cache, "q": to_dev(np.ascontiguousarray(w.q[0]), "bf16"),
+                                  "page_table": pt, "length": L + W, "out": ver[0].astype(np.float32), "sigma": sig}
+    return refs
 
 
 def test_tuner_reference_gate_and_install():
     hq, hkv, D, W = 16, 4, 64, 3
-    w, ref = _reference(hq, hkv, D, W, 1500, seed=77)
+    refs = _references(hq, hkv, D, W, 512, 3000, seed=77)
     dcfg, vcfg, rep, _ = _tune(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, n_draft=W, ctx_small=512,
-                               ctx_large=8192, budget_ms=6000, seed=3, install=True, ref=ref)
+                               ctx_large=8192, budget_ms=6000, seed=3, install=True, refs=refs,
+                               ref_tol=ATOL_SIGMA)
     assert rep["installed"]
     for unit, cands in zip(rep["units"], rep["candidates"]):
-        assert unit["qualified"]
+        assert unit["qualified"] and unit["oracle_gate"] == [True, True]
         for c in cands:
             if c["verdict"] == "admitted":
-                assert c["ref_dev"] <= ATOL_SIGMA
+                assert max(c["ref_dev"]) <= ATOL_SIGMA
     # installed winners serve calls without a config, still at parity
     _parity(None, hq, hkv, D, 1)
     _parity(None, hq, hkv, D, W)
@@ -119,15 +136,30 @@ def test_tuner_reference_gate_and_install():
 
 def test_tuner_wrong_references_admit_nothing():
     hq, hkv, D, W = 8, 8, 64, 2
-    w, ref = _reference(hq, hkv, D, W, 700, seed=78)
-    ref["out"] = ref["out"] + 0.5            # references planted wrong on the host
-    ref["out_verify"] = ref["out_verify"] + 0.5
+    refs = _references(hq, hkv, D, W, 300, 700, seed=78)
+    for r in refs.values():
+        r["out"] = r["out"] + 0.5            # references planted wrong on the host
     dcfg, vcfg, rep, _ = _tune(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, n_draft=W, ctx_small=512,
-                               ctx_large=4096, budget_ms=4000, seed=4, install=True, ref=ref)
+                               ctx_large=4096, budget_ms=4000, seed=4, install=True, refs=refs,
+                               ref_tol=ATOL_SIGMA)
     assert dcfg.qualified == 0 and vcfg.qualified == 0
     for unit, cands in zip(rep["units"], rep["candidates"]):
         assert not unit["qualified"] and unit["admitted"] == 0
-        assert cands[0]["verdict"] == "rejected"
+        assert cands[0]["verdict"] == "rejected" and cands[0]["gate"] == "oracle"
+
+
+def test_tuner_one_wrong_term_rejects_the_unit():
+    """Every term is gated: a reference wrong on the large verify term alone
+    leaves the verify unit unqualified and the decode unit qualified."""
+    hq, hkv, D, W = 8, 2, 128, 4
+    refs = _references(hq, hkv, D, W, 300, 1200, seed=79)
+    refs["verify_large"]["out"] = refs["verify_large"]["out"] * 1.01 + 0.05
+    dcfg, vcfg, rep, _ = _tune(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, n_draft=W, ctx_small=512,
+                               ctx_large=4096, budget_ms=4000, seed=5, refs=refs,
+                               ref_tol=ATOL_SIGMA)
+    assert dcfg.qualified == 1 and vcfg.qualified == 0
+    ver = rep["candidates"][1][0]
+    assert ver["verdict"] == "rejected" and ver["gate"] == "oracle" and "term 3" in ver["why"]
 
 
 def test_tuner_search_order_follows_virtual_completion_time():

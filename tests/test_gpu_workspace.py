@@ -2,9 +2,10 @@
 units (blog.123qwe.co.kr/?p=3927, section 5) run split-K here, with a
 log-sum-exp merge of the split records.  Splits past a sequence's last page
 never write their records, so the merge must mask them rather than read
-them.  The workspace is filled with 0xFF bytes (every float a NaN) before
-each call; ragged batches with empty, one-token and long sequences leave
-many such records."""
+them.  The workspace's records are filled with 0xFF bytes (every float a
+NaN) before each call, its header (the in-launch merge's counters) zeroed
+as the contract asks; ragged batches with empty, one-token and long
+sequences leave many such records."""
 
 import numpy as np
 import pytest
@@ -15,10 +16,15 @@ from tests.util import ATOL_SIGMA, normalized_err, oracle_out
 pytestmark = pytest.mark.gpu
 
 
+WS_HEADER = 65536        # Q8K4V_WS_HEADER_BYTES: zero before first use (the contract)
+
+
 def _nan_workspace(nbytes):
+    """The header zeroed as the contract asks, every record byte 0xFF."""
     import torch
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     ws.fill_(0xFF)
+    ws[:WS_HEADER].zero_()
     return ws
 
 
@@ -30,7 +36,7 @@ def _check(w, got, want, label):
 
 
 @pytest.mark.parametrize("n_draft", [0, 4])
-@pytest.mark.parametrize("cfg", [None, dict(variant=3), dict(split_pages=4)], ids=str)
+@pytest.mark.parametrize("cfg", [None, dict(variant=5), dict(split_pages=4), dict(fused_combine=1)], ids=str)
 def test_garbage_workspace_decode_and_verify(n_draft, cfg):
     import torch
     import decode_attention_quantized_kv_amd as q8

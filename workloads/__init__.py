@@ -16,7 +16,12 @@ multi-session suffix lengths come from ``default_rng(seed + 1000)``):
   by bit arithmetic and hand the bit patterns over;
 * physical page ids are a seeded permutation of the pool, so logical order
   and physical order differ; in the multi-session workload every session maps
-  the same shared prefix pages first, then private suffix pages.
+  the same shared prefix pages first, then private suffix pages;
+* optional query dynamic range (from its own stream, ``default_rng(seed +
+  2000)``, so the draws above are unchanged): ``q_outlier`` multiplies
+  ``round(0.01 * Hq * D)`` (query head, dim) channels, drawn without
+  replacement, by that factor in every query row; ``q_decades`` multiplies
+  every query element by 10 ** U(-q_decades / 2, q_decades / 2).
 """
 
 from __future__ import annotations
@@ -95,7 +100,7 @@ def _encode(x: np.ndarray, dtype: str) -> np.ndarray:
 def build(name: str, *, seed: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
           dtype: str, seq_lens, n_draft: int = 0, outliers: bool = False,
           shared_prefix: int = 0, permute_pages: bool = True, spare_pages: int = 0,
-          value_scale: float = 1.0) -> Workload:
+          value_scale: float = 1.0, q_outlier: float = 0.0, q_decades: float = 0.0) -> Workload:
     """Generic builder.  ``seq_lens`` counts cached tokens per sequence
     (drafts included for verify).  With ``shared_prefix`` > 0 (a multiple of
     16) every sequence maps the same prefix pages; each sequence's own tokens
@@ -143,6 +148,18 @@ def build(name: str, *, seed: int, num_q_heads: int, num_kv_heads: int, head_dim
         n = per_seq_pages[b]
         page_table[b, pre_pages:pre_pages + n] = perm[nxt:nxt + n]
         nxt += n
+
+    # -- query dynamic range (own stream) ------------------------------------
+    if q_outlier or q_decades:
+        qrng = np.random.default_rng(seed + 2000)
+        if q_outlier:
+            n = int(round(0.01 * Hq * D))
+            idx = qrng.choice(Hq * D, size=n, replace=False)
+            m = np.ones(Hq * D, np.float32)
+            m[idx] = np.float32(q_outlier)
+            q *= m.reshape(Hq, D)
+        if q_decades:
+            q *= (10.0 ** qrng.uniform(-q_decades / 2, q_decades / 2, size=q.shape)).astype(np.float32)
 
     # -- append batches ------------------------------------------------------
     appends = []
@@ -218,6 +235,16 @@ def multi_session(seed: int = 4, sessions: int = 16, prefix: int = 32768,
     return build(f"multi_session_{sessions}x{prefix}", seed=seed, num_q_heads=32, num_kv_heads=4,
                  head_dim=128, dtype="bf16", seq_lens=prefix + suffix, outliers=True,
                  shared_prefix=prefix)
+
+
+def tune_reference(context: int, n_draft: int = 8, seed: int = 11) -> Workload:
+    """Caller inputs of the tuner's oracle gate at one context: one sequence
+    of ``context`` cached tokens plus ``n_draft`` drafts (32 query / 8 kv
+    heads, D 128, bf16, 1 % outlier channels x8).  The decode term attends
+    the first ``context`` tokens with draft 0's query, the verify term all of
+    them with every draft."""
+    return build(f"tune_ref_{context}_w{n_draft}", seed=seed, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                 dtype="bf16", seq_lens=[context + n_draft], n_draft=n_draft, outliers=True)
 
 
 NAMED = {
