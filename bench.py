@@ -353,17 +353,29 @@ def run_probes(torch, q8, caches, seq_lens, msl, page_table, K, layers, cache_re
 
     res = {"paged_bytes": cache_read}
     if not n_pref:   # the probe streams each sequence's own pages (a shared prefix would be re-read)
-        best = None
-        for waves, stages in ((4, 2), (4, 3), (4, 4), (8, 2), (8, 3)):
-            ms = time_graph(lambda i: q8.hbm_probe(caches[i % layers], seq_lens, msl, page_table, waves, stages),
+        best, best_grouped = None, None
+        H = caches[0].num_kv_heads
+        shapes = [(4, 2, 1), (4, 3, 1), (4, 4, 1), (8, 2, 1), (8, 3, 1),
+                  (4, 3, 2), (4, 3, 4), (8, 3, 2), (8, 3, 4), (8, 2, 8), (8, 3, 8)]
+        for waves, stages, hpw in shapes:
+            if H % hpw:
+                continue
+            ms = time_graph(lambda i: q8.hbm_probe(caches[i % layers], seq_lens, msl, page_table, waves, stages, hpw),
                             min(K, 4 * layers))
             gbs = cache_read / (ms * 1e-3) / 1e9
-            res[f"paged_GBs_w{waves}s{stages}"] = round(gbs, 1)
-            if best is None or gbs > best[0]:
+            res[f"paged_GBs_w{waves}s{stages}h{hpw}"] = round(gbs, 1)
+            if hpw == 1 and (best is None or gbs > best[0]):
                 best = (gbs, ms, waves, stages)
+            if hpw > 1 and (best_grouped is None or gbs > best_grouped[0]):
+                best_grouped = (gbs, ms, waves, stages, hpw)
+        # the decode kernel's own mapping (one kv head per workgroup)
         res["paged_GBs"] = round(best[0], 1)
         res["paged_us"] = round(best[1] * 1e3, 3)
         res["paged_shape"] = {"waves_per_wg": best[2], "stages": best[3]}
+        if best_grouped:
+            res["paged_grouped_GBs"] = round(best_grouped[0], 1)
+            res["paged_grouped_shape"] = {"waves_per_wg": best_grouped[2], "stages": best_grouped[3],
+                                          "heads_per_wg": best_grouped[4]}
     seg = 256 << 20
     buf = torch.empty(8 * seg, dtype=torch.uint8, device="cuda:0")
     ms = time_graph(lambda i: q8.stream_probe(buf[(i % 8) * seg:(i % 8 + 1) * seg], 8, 3), 16)

@@ -119,7 +119,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.tune_select.restype = i32
     lib.tune_select.argtypes = [C.POINTER(TuneRequest), C.POINTER(Config), C.c_char_p, sz]
     lib.q8k4v_hbm_probe.restype = i32
-    lib.q8k4v_hbm_probe.argtypes = [C.POINTER(CacheDesc), i32, vp, i32, vp, i32, i32, i32, vp]
+    lib.q8k4v_hbm_probe.argtypes = [C.POINTER(CacheDesc), i32, vp, i32, vp, i32, i32, i32, i32, vp]
     lib.q8k4v_stream_probe.restype = i32
     lib.q8k4v_stream_probe.argtypes = [vp, sz, i32, i32, vp]
     _lib = lib
@@ -426,14 +426,15 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
 
 
 def hbm_probe(cache: PagedKVCache, seq_lens, max_seq_len: int, page_table, waves_per_wg: int = 4,
-              stages: int = 3, stream=None) -> None:
+              stages: int = 3, heads_per_wg: int = 1, stream=None) -> None:
     """Streams the page-head blocks a decode launch over ``cache`` reads
     (same split and mapping, HBM -> LDS, no compute): the memory system's
-    rate for that access pattern."""
+    rate for that access pattern.  ``heads_per_wg`` > 1 streams that many
+    kv heads of each page per workgroup."""
     lib = load_library()
     rc = lib.q8k4v_hbm_probe(C.byref(cache.desc), int(seq_lens.shape[0]), _ptr(seq_lens, "seq_lens", i32=True),
                              int(max_seq_len), _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
-                             int(waves_per_wg), int(stages), _stream(stream))
+                             int(waves_per_wg), int(stages), int(heads_per_wg), _stream(stream))
     _check("q8k4v_hbm_probe", rc)
 
 

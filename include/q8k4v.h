@@ -343,12 +343,17 @@ int32_t attn_prefill_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dt
  *                 attn_decode_q8k4v (symmetric codec only)
  *   waves_per_wg, stages: launch shape, (4, 2..4) or (8, 2..3); stages - 1
  *                 tiles per wave in flight
+ *   heads_per_wg  1: the decode kernel's mapping (one kv head per
+ *                 workgroup); 2, 4 or 8 (8 with 8 waves): as many workgroups,
+ *                 each streaming that many kv heads of 1/heads_per_wg of
+ *                 the pages, so the heads' blocks of a page (contiguous in
+ *                 every pool) are read by one compute unit together
  * Errors: EINVAL (shape, codec, launch shape), EHIP.  Writes nothing to
  * device memory.
  */
 int32_t q8k4v_hbm_probe(const q8k4v_cache *cache, int32_t n_seqs, const int32_t *seq_lens,
                         int32_t max_seq_len, const int32_t *page_table, int32_t max_pages,
-                        int32_t waves_per_wg, int32_t stages, hipStream_t stream);
+                        int32_t waves_per_wg, int32_t stages, int32_t heads_per_wg, hipStream_t stream);
 
 /*
  * q8k4v_stream_probe -- the sequential reference: streams `bytes` of the

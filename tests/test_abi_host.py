@@ -242,10 +242,12 @@ def test_long_context_splits_are_even(lib):
 def test_probes_reject_bad_arguments(lib):
     """The streaming probes validate before any launch."""
     d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1)
-    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 4, 5, None) == -1       # stages
-    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 2, 2, None) == -1       # waves
+    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 4, 5, 1, None) == -1       # stages
+    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 2, 2, 1, None) == -1       # waves
+    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 4, 3, 8, None) == -1       # 8 heads need 8 waves
+    assert lib.q8k4v_hbm_probe(C.byref(d), 1, 1, 1024, 1, 64, 4, 3, 3, None) == -1       # heads per workgroup
     da = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1, q8.CODEC_AFFINE, 1, 1)
-    assert lib.q8k4v_hbm_probe(C.byref(da), 1, 1, 1024, 1, 64, 4, 3, None) == -1      # symmetric only
+    assert lib.q8k4v_hbm_probe(C.byref(da), 1, 1, 1024, 1, 64, 4, 3, 1, None) == -1      # symmetric only
     assert lib.q8k4v_stream_probe(None, 4096, 4, 3, None) == -1
     assert lib.q8k4v_stream_probe(16, 1000, 4, 3, None) == -1                         # too short
     assert lib.q8k4v_stream_probe(16, 4100, 4, 3, None) == -1                         # not a multiple of 16
