@@ -118,6 +118,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
                                       C.c_float, C.POINTER(Config), vp, sz, vp]
     lib.tune_select.restype = i32
     lib.tune_select.argtypes = [C.POINTER(TuneRequest), C.POINTER(Config), C.c_char_p, sz]
+    lib.attn_decode_q8k4v_noalloc.restype = i32
+    lib.attn_decode_q8k4v_noalloc.argtypes = [C.POINTER(CacheDesc), vp, i32, vp, i32, i32, vp, i32, vp, i32,
+                                              C.c_float, C.POINTER(Config), vp]
     lib.q8k4v_hbm_probe.restype = i32
     lib.q8k4v_hbm_probe.argtypes = [C.POINTER(CacheDesc), i32, vp, i32, vp, i32, i32, i32, i32, vp]
     lib.q8k4v_stream_probe.restype = i32
@@ -268,6 +271,28 @@ def attn_decode_q8k4v(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_t
                                float(softmax_scale), C.byref(cfg) if cfg is not None else None,
                                _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("attn_decode_q8k4v", rc)
+    return out
+
+
+def attn_decode_q8k4v_noalloc(cache: PagedKVCache, q, seq_lens, max_seq_len: int, page_table,
+                              softmax_scale: Optional[float] = None, out=None, cfg: Optional[Config] = None,
+                              stream=None):
+    """:func:`attn_decode_q8k4v` without a workspace argument: the library's
+    static per-GPU scratch array holds the split records (the call
+    allocates no device memory; ``out`` should be passed to keep it so)."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    rc = lib.attn_decode_q8k4v_noalloc(C.byref(cache.desc), _ptr(q, "q"), _dtype_code(q), _ptr(out, "out"), B, Hq,
+                                       _ptr(seq_lens, "seq_lens", i32=True), int(max_seq_len),
+                                       _ptr(page_table, "page_table", i32=True), int(page_table.shape[1]),
+                                       float(softmax_scale), C.byref(cfg) if cfg is not None else None,
+                                       _stream(stream))
+    _check("attn_decode_q8k4v_noalloc", rc)
     return out
 
 
@@ -448,7 +473,8 @@ def stream_probe(buf, waves_per_wg: int = 4, stages: int = 3, stream=None) -> No
 
 
 __all__ = ["kv_quant_append", "attn_decode_q8k4v", "attn_decode_prefix_q8k4v", "attn_verify_q8k4v",
-           "attn_prefill_q8k4v", "attn_decode_append_q8k4v", "tune_select", "hbm_probe", "stream_probe",
+           "attn_prefill_q8k4v", "attn_decode_append_q8k4v", "attn_decode_q8k4v_noalloc", "tune_select",
+           "hbm_probe", "stream_probe",
            "TUNE_TERMS",
            "workspace_bytes", "prefix_workspace_bytes",
            "PagedKVCache", "Config", "make_config", "load_library", "version", "Q8K4VError", "LIB_PATH"]

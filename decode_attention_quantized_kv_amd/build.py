@@ -25,7 +25,7 @@ OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libq8k4v.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "q8k4v")
 
-SOURCES = ["abi.cpp", "append.hip", "attn_paged.hip", "combine.hip", "probe.hip", "tuner.cpp"]
+SOURCES = ["abi.cpp", "append.hip", "attn_paged.hip", "combine.hip", "noalloc.cpp", "probe.hip", "tuner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

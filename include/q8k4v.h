@@ -306,6 +306,30 @@ int32_t attn_decode_append_q8k4v(const q8k4v_cache *cache, const void *k_new, co
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_q8k4v_noalloc -- attn_decode_q8k4v without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * split records and the in-launch merge's counters live in a static device
+ * array of Q8K4V_NOALLOC_SCRATCH_BYTES per GPU, inside the library, held
+ * until the process ends; the call allocates nothing.  The first call on a
+ * device looks the array up (hipGetSymbolAddress) and clears its counter
+ * header with a fill kernel enqueued on `stream` before the attention work.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads) race and give undefined output; calls
+ * serialised on one stream do not.
+ * Arguments, results and the other errors as attn_decode_q8k4v; EWORKSPACE
+ * when the launch needs more scratch than the array holds (16 MiB: the
+ * 64 KiB header plus 31,651 split records -- one per sequence, kv head,
+ * split and query row -- at D = 128; the 64K decode takes 1,024).
+ */
+#define Q8K4V_NOALLOC_SCRATCH_BYTES (16u << 20)
+int32_t attn_decode_q8k4v_noalloc(const q8k4v_cache *cache, const void *q, int32_t q_dtype,
+                                  float *out, int32_t n_seqs, int32_t num_q_heads,
+                                  const int32_t *seq_lens, int32_t max_seq_len,
+                                  const int32_t *page_table, int32_t max_pages, float softmax_scale,
+                                  const q8k4v_config *cfg, hipStream_t stream);
+
+/*
  * attn_prefill_q8k4v -- chunked-prefill attention over the quantized cache:
  * n_new new tokens per sequence (already appended) attend the cache, causal
  * among themselves -- the computation of attn_verify_q8k4v for chunks of up
