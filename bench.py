@@ -40,6 +40,7 @@ HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 WORKLOADS = ["tiny_decode_256", "gqa_decode_4096", "gqa_decode_65536", "verify_65536_w8", "multi_session_16x32768"]
 TUNE_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q8kv_d128_w8.npz")
+TUNE_SESSION_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q4kv_d128_s16.npz")
 
 
 def cache_bytes_per_token_head(D: int, affine: bool = False) -> int:
@@ -102,17 +103,22 @@ def main() -> int:
     cfg = q8.make_config(**json.loads(args.config)) if args.config else None
     tuned = None
     if args.tune:
-        dcfg, vcfg, rep = run_tuner(torch, q8, workloads, args.tune_budget_ms)
+        # the multi-session workload (32 q / 4 kv heads) tunes with its
+        # session unit; the others at 32 q / 8 kv heads
+        sessions = args.workload == "multi_session_16x32768"
+        dcfg, vcfg, mcfg, rep = run_tuner(torch, q8, workloads, args.tune_budget_ms, sessions)
         if args.tune_report:
             with open(args.tune_report, "w") as f:
                 json.dump(rep, f)
         w0 = workloads.NAMED[args.workload if args.workload != "all" else "gqa_decode_65536"]()
-        cfg = vcfg if w0.n_draft else dcfg
+        cfg = mcfg if sessions else vcfg if w0.n_draft else dcfg
         tuned = {"decode": dcfg.as_dict(), "verify": vcfg.as_dict(),
                  "status": rep.get("status"), "units": [{k: u.get(k) for k in
                                                           ("unit", "qualified", "chosen_cost", "oracle_gate",
                                                            "admitted", "rejected", "rejected_by", "invalid")}
                                                          for u in rep.get("units", [])]}
+        if sessions:
+            tuned["multi_session"] = mcfg.as_dict()
 
     names = WORKLOADS if args.workload == "all" else [args.workload]
     for name in names:
@@ -124,29 +130,51 @@ def main() -> int:
     return 0
 
 
-def run_tuner(torch, q8, workloads, budget_ms):
+def run_tuner(torch, q8, workloads, budget_ms, sessions=False):
     """tune_select over decode / verify at 4096 and 65536 tokens (32 q / 8 kv
     heads, D 128, 8 drafts), each term gated by the oracle outputs stored in
-    tests/golden (written by tests/golden/make_tune_refs.py) at 2e-3 sigma."""
-    z = np.load(TUNE_REFS)
+    tests/golden (written by tests/golden/make_tune_refs.py) at 2e-3 sigma.
+    With ``sessions``: at 32 q / 4 kv heads with the 16-session unit, whose
+    two terms are gated the same way (the decode / verify units there by the
+    alpha gate alone)."""
     refs = {}
     keep = []
-    for size, ctx, seed in (("small", 4096, 11), ("large", 65536, 12)):
-        w = workloads.tune_reference(ctx, 8, seed)
-        cache = q8.PagedKVCache(w.num_pages, w.num_kv_heads, w.head_dim)
-        for a in w.appends:
-            q8.kv_quant_append(cache, _dev(torch, a.k, True), _dev(torch, a.v, True), _dev(torch, a.cu_new),
-                               _dev(torch, a.start_pos), _dev(torch, a.page_table))
-        pt = _dev(torch, np.ascontiguousarray(w.page_table[0]))
-        keep.append(cache)
-        sigma = z["sigma_" + size]
-        refs["decode_" + size] = {"cache": cache, "q": _dev(torch, np.ascontiguousarray(w.q[0, 0]), True),
-                                  "page_table": pt, "length": ctx, "out": z["decode_" + size], "sigma": sigma}
-        refs["verify_" + size] = {"cache": cache, "q": _dev(torch, np.ascontiguousarray(w.q[0]), True),
-                                  "page_table": pt, "length": ctx + 8, "out": z["verify_" + size], "sigma": sigma}
+    if not sessions:
+        z = np.load(TUNE_REFS)
+        for size, ctx, seed in (("small", 4096, 11), ("large", 65536, 12)):
+            w = workloads.tune_reference(ctx, 8, seed)
+            cache = _upload(torch, q8, w)
+            pt = _dev(torch, np.ascontiguousarray(w.page_table[0]))
+            keep.append(cache)
+            sigma = z["sigma_" + size]
+            refs["decode_" + size] = {"cache": cache, "q": _dev(torch, np.ascontiguousarray(w.q[0, 0]), True),
+                                      "page_table": pt, "length": ctx, "out": z["decode_" + size], "sigma": sigma}
+            refs["verify_" + size] = {"cache": cache, "q": _dev(torch, np.ascontiguousarray(w.q[0]), True),
+                                      "page_table": pt, "length": ctx + 8, "out": z["verify_" + size],
+                                      "sigma": sigma}
+    else:
+        z = np.load(TUNE_SESSION_REFS)
+        for size, ctx, seed in (("small", 4096, 13), ("large", 65536, 14)):
+            w = workloads.tune_sessions_reference(ctx, 16, seed)
+            cache = _upload(torch, q8, w)
+            keep.append(cache)
+            refs["multi_session_" + size] = {
+                "cache": cache, "q": _dev(torch, w.q, True), "page_table": _dev(torch, w.page_table),
+                "length": int(w.seq_lens.max()), "seq_lens": _dev(torch, w.seq_lens),
+                "n_prefix_pages": w.shared_prefix // 16, "out": z["multi_session_" + size],
+                "sigma": z["sigma_" + size]}
     torch.cuda.synchronize()
-    return q8.tune_select(32, 8, 128, n_draft=8, ctx_small=4096, ctx_large=65536, budget_ms=budget_ms,
-                          install=True, refs=refs, ref_tol=2e-3)
+    return q8.tune_select(32, 4 if sessions else 8, 128, n_draft=8, ctx_small=4096, ctx_large=65536,
+                          budget_ms=budget_ms, install=True, refs=refs, ref_tol=2e-3,
+                          n_sessions=16 if sessions else 0)
+
+
+def _upload(torch, q8, w):
+    cache = q8.PagedKVCache(w.num_pages, w.num_kv_heads, w.head_dim)
+    for a in w.appends:
+        q8.kv_quant_append(cache, _dev(torch, a.k, True), _dev(torch, a.v, True), _dev(torch, a.cu_new),
+                           _dev(torch, a.start_pos), _dev(torch, a.page_table))
+    return cache
 
 
 def _dev(torch, a, bf=False):

@@ -57,21 +57,23 @@ class Config(C.Structure):
 
 class TuneRef(C.Structure):
     _fields_ = [("cache", C.POINTER(CacheDesc)), ("q", C.c_void_p), ("page_table", C.c_void_p),
-                ("len", C.c_int32), ("max_pages", C.c_int32), ("out", C.c_void_p), ("sigma", C.c_void_p)]
+                ("len", C.c_int32), ("max_pages", C.c_int32), ("out", C.c_void_p), ("sigma", C.c_void_p),
+                ("seq_lens", C.c_void_p), ("n_seqs", C.c_int32), ("n_prefix_pages", C.c_int32)]
 
 
 class TuneRequest(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("n_draft", C.c_int32), ("ctx_small", C.c_int32), ("ctx_large", C.c_int32),
                 ("budget_ms", C.c_int64), ("mem_cap_bytes", C.c_size_t), ("seed", C.c_uint64),
-                ("install", C.c_int32), ("max_candidates", C.c_int32),
-                ("ref", TuneRef * 4), ("ref_tol", C.c_float),
+                ("install", C.c_int32), ("max_candidates", C.c_int32), ("n_sessions", C.c_int32),
+                ("ref", TuneRef * 6), ("ref_tol", C.c_float),
                 ("softmax_scale", C.c_float), ("record_path", C.c_char_p)]
 
 
-# the four terms of the tuner's service cost, in the order of
-# q8k4v_tune_request.ref
-TUNE_TERMS = ("decode_small", "decode_large", "verify_small", "verify_large")
+# the terms of the tuner's service cost, in the order of
+# q8k4v_tune_request.ref (the last two with n_sessions >= 2 only)
+TUNE_TERMS = ("decode_small", "decode_large", "verify_small", "verify_large",
+              "multi_session_small", "multi_session_large")
 
 
 _lib = None
@@ -401,22 +403,28 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
                 ctx_small: int = 4096, ctx_large: int = 65536, budget_ms: int = 60000,
                 mem_cap_bytes: int = 0, seed: int = 0, install: bool = False, max_candidates: int = 0,
                 refs=None, ref_tol: float = 0.0, report_cap: int = 1 << 20,
-                record_path: Optional[str] = None):
-    """Runs the on-device tuner.  ``refs`` (optional): a dict keyed by
-    :data:`TUNE_TERMS` (``decode_small``, ``decode_large``, ``verify_small``,
-    ``verify_large``), each a dict with ``cache`` (PagedKVCache), ``q``
-    (device bf16 ``[n][Hq][D]``), ``page_table`` (device int32, one
-    sequence's pages), ``length``, ``out`` (host float32 ``[n][Hq][D]``,
-    the expected output) and optionally ``sigma`` (host ``[Hq][D]``, which
-    normalises the deviation); ``ref_tol`` bounds it.  ``record_path`` (optional): file of
-    stored choices, reused for the same device identity and request shape.
-    Returns (decode Config, verify Config, report dict)."""
+                record_path: Optional[str] = None, n_sessions: int = 0):
+    """Runs the on-device tuner.  ``n_sessions`` >= 2 adds the multi-session
+    unit (the shared-prefix entry point's suffix pass over that many
+    sessions).  ``refs`` (optional): a dict keyed by :data:`TUNE_TERMS`, each a
+    dict with ``cache`` (PagedKVCache), ``q`` (device bf16 ``[n][Hq][D]``),
+    ``page_table`` (device int32: one sequence's pages, or ``[n_seqs][max_pages]``
+    for the multi-session terms), ``length`` (tokens attended; the longest
+    session for the multi-session terms), ``out`` (host float32
+    ``[n][Hq][D]``, the expected output) and optionally ``sigma`` (host
+    ``[Hq][D]``, which normalises the deviation); the multi-session terms also
+    take ``seq_lens`` (device int32 ``[n_seqs]``) and ``n_prefix_pages``.
+    ``ref_tol`` bounds the normalised deviation.  ``record_path`` (optional):
+    file of stored choices, reused for the same device identity and request
+    shape.  Returns (decode Config, verify Config, multi-session Config or
+    None, report dict)."""
     import numpy as np
     lib = load_library()
     req = TuneRequest()
     req.num_q_heads, req.num_kv_heads, req.head_dim, req.n_draft = num_q_heads, num_kv_heads, head_dim, n_draft
     req.ctx_small, req.ctx_large, req.budget_ms = ctx_small, ctx_large, budget_ms
     req.mem_cap_bytes, req.seed, req.install, req.max_candidates = mem_cap_bytes, seed, int(install), max_candidates
+    req.n_sessions = int(n_sessions)
     keep = []
     for k, term in enumerate(TUNE_TERMS):
         r = (refs or {}).get(term)
@@ -429,16 +437,20 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
         req.ref[k].q = _ptr(r["q"], "q").value
         req.ref[k].page_table = _ptr(pt, "page_table", i32=True).value
         req.ref[k].len = int(r["length"])
-        req.ref[k].max_pages = int(pt.numel())
+        req.ref[k].max_pages = int(pt.shape[-1])
         req.ref[k].out = out.ctypes.data
         if r.get("sigma") is not None:
             sig = np.ascontiguousarray(r["sigma"], dtype=np.float32)
             keep.append(sig)
             req.ref[k].sigma = sig.ctypes.data
+        if k >= 4:
+            req.ref[k].seq_lens = _ptr(r["seq_lens"], "seq_lens", i32=True).value
+            req.ref[k].n_seqs = int(r["seq_lens"].shape[0])
+            req.ref[k].n_prefix_pages = int(r["n_prefix_pages"])
     req.ref_tol = float(ref_tol)
     if record_path is not None:
         req.record_path = os.fsencode(record_path)
-    table = (Config * 2)()
+    table = (Config * 3)()
     buf = C.create_string_buffer(report_cap)
     rc = lib.tune_select(C.byref(req), table, buf, report_cap)
     _check("tune_select", rc)
@@ -447,7 +459,7 @@ def tune_select(num_q_heads: int, num_kv_heads: int, head_dim: int, n_draft: int
         report = json.loads(text) if text else {}
     except json.JSONDecodeError:
         report = {"raw": text}
-    return table[0], table[1], report
+    return table[0], table[1], (table[2] if n_sessions >= 2 else None), report
 
 
 def hbm_probe(cache: PagedKVCache, seq_lens, max_seq_len: int, page_table, waves_per_wg: int = 4,

@@ -414,6 +414,23 @@ int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp,
     return launch_combine_cascade(suf, D, stream);
 }
 
+q8k4v_config cascade_default_config(int32_t group) {
+    q8k4v_config c = default_config(std::max(1, group));
+    c.wgs_per_cu = kCascadeSuffixWgsPerCu;
+    return c;
+}
+
+// Suffix-pass configuration of the cascade: the caller's, else the one
+// tune_select installed for this device and head shape, else the decode
+// defaults with more, shorter splits (ragged suffixes balance better).
+static const q8k4v_config* cascade_config(const q8k4v_config* cfg, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, q8k4v_config* dflt) {
+    if (cfg || num_kv_heads <= 0) return cfg;
+    if (tuned_lookup(kTunedCascadeKey, num_q_heads, num_kv_heads, head_dim, dflt)) return dflt;
+    *dflt = cascade_default_config(num_q_heads / num_kv_heads);
+    return dflt;
+}
+
 }  // namespace q8k4v
 
 using namespace q8k4v;
@@ -480,22 +497,13 @@ size_t q8k4v_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv
     return plan_workspace(p);
 }
 
-// Suffix-pass configuration of the cascade: the caller's, else the decode
-// defaults with more, shorter splits (ragged suffixes balance better).
-static const q8k4v_config* cascade_config(const q8k4v_config* cfg, int32_t num_q_heads, int32_t num_kv_heads,
-                                          q8k4v_config* dflt) {
-    if (cfg || num_kv_heads <= 0) return cfg;
-    *dflt = default_config(std::max(1, num_q_heads / num_kv_heads));
-    dflt->wgs_per_cu = kCascadeSuffixWgsPerCu;
-    return dflt;
-}
 
 size_t q8k4v_prefix_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_seq_len, int32_t n_prefix_pages, const q8k4v_config* cfg) {
     if (n_prefix_pages == 0)
         return q8k4v_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, 0, cfg);
     q8k4v_config dflt;
-    cfg = cascade_config(cfg, num_q_heads, num_kv_heads, &dflt);
+    cfg = cascade_config(cfg, num_q_heads, num_kv_heads, head_dim, &dflt);
     // the larger need of the codecs the configuration supports (a plan
     // unavailable for one codec does not count)
     size_t need = 0;
@@ -552,7 +560,7 @@ int32_t attn_decode_prefix_q8k4v(const q8k4v_cache* cache, const void* q, int32_
     AttnArgs a{cache, q, q_dtype, out, n_seqs, num_q_heads, 1, seq_lens, max_seq_len,
                page_table, max_pages, softmax_scale};
     q8k4v_config dflt;
-    cfg = cascade_config(cfg, num_q_heads, cache ? cache->num_kv_heads : 0, &dflt);
+    cfg = cascade_config(cfg, num_q_heads, cache ? cache->num_kv_heads : 0, cache ? cache->head_dim : 0, &dflt);
     CascadePlan cp;
     int32_t rc = make_plan(a, cfg, &cp.suf);        // validates the shape as a decode launch
     if (rc == Q8K4V_OK) rc = make_cascade_plan(a, n_prefix_pages, cfg, &cp);

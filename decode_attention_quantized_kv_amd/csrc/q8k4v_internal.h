@@ -90,6 +90,11 @@ struct CascadePlan {
 };
 constexpr int32_t kMaxPrefixRows = 4096;
 constexpr int32_t kCascadeSuffixWgsPerCu = 4;   // suffix pass, when the caller gives no config
+// Default suffix-pass configuration of the cascade for `group` query heads
+// per kv head (the decode defaults with kCascadeSuffixWgsPerCu).
+q8k4v_config cascade_default_config(int32_t group);
+// Key of the multi-session unit in the tuned table (decode is n_draft 1).
+constexpr int32_t kTunedCascadeKey = 0;
 int32_t make_cascade_plan(const AttnArgs& a, int32_t n_prefix_pages, const q8k4v_config* cfg, CascadePlan* cp);
 size_t cascade_workspace(const CascadePlan& cp);
 int32_t launch_cascade(const AttnArgs& a, int32_t n_prefix_pages, const CascadePlan& cp, void* workspace,

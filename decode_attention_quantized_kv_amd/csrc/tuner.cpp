@@ -6,7 +6,10 @@
 // admission, synthesis of the timing caches on the device, the defaults'
 // measurements and outputs, the storage-resolution noise, the candidates and
 // their gate.  Per unit (decode: one query row block per kv head; verify:
-// n_draft drafts) the service cost of a configuration c is
+// n_draft drafts; with n_sessions, multi-session: the shared-prefix entry
+// point's suffix pass, ns sessions over a ctx / 2 token shared prefix with
+// private suffixes of about (i + 1) / ns x ctx / 2 tokens) the service cost
+// of a configuration c is
 //     cost(c) = sum over the unit's two shapes p of median(c, p) / median(default, p)
 // with shapes at ctx_small and ctx_large, term weights 1, one launch per
 // layer-step.  Times are per launch within a replayed graph of launches on
@@ -36,8 +39,8 @@
 // configuration's output by at most alpha = 8 times the storage-resolution
 // noise -- the change of the default output when every stored code moves by
 // one quantisation step -- and, on every term for which the caller passes a
-// reference output (decode and verify at both contexts, e.g. computed by a
-// CPU oracle on the caller's inputs), the sigma-normalised deviation from it
+// reference output (decode, verify and multi-session at both contexts, e.g.
+// computed by a CPU oracle on the caller's inputs), the sigma-normalised deviation from it
 // may not exceed ref_tol.  A deviation that was not measured is reported as
 // unknown (null), never as 0.
 #include <hip/hip_runtime.h>
@@ -135,11 +138,16 @@ __global__ void fill_bf16_kernel(uint16_t* q, size_t n, uint64_t seed) {
 
 // ---- host side --------------------------------------------------------------
 
+constexpr int kUnits = 3;          // decode, verify, multi-session
+constexpr int kMaxSessions = 64;
+
 struct Shape {
     std::string name;
-    int n_draft;       // 1 for decode
-    int ctx;           // cached tokens (drafts included for verify)
-    bool small;
+    int kind = 0;      // 0 decode, 1 verify, 2 sessions over a shared prefix (the cascade)
+    int n_draft = 1;   // 1 for decode and the cascade
+    int ctx = 0;       // cached tokens (drafts included for verify); the longest session
+    bool small = false;
+    int n_seqs = 1, n_pref = 0, max_pages = 0;   // the cascade's sessions, shared pages, table row length
 };
 
 constexpr double kUnmeasured = NAN;   // printed as null ("unknown")
@@ -154,8 +162,8 @@ struct Cand {
     double dev[2] = {kUnmeasured, kUnmeasured};   // max |out - default out| per shape
     double ref_dev[2] = {kUnmeasured, kUnmeasured};   // normalised deviation from the unit's references
     double cost = kUnmeasured;
-    int seq = -1;                  // position in the measurement order (both units)
-    double vt[2] = {-1, -1};       // virtual completion times of the units when it was picked
+    int seq = -1;                  // position in the measurement order (all units)
+    double vt[kUnits] = {-1, -1, -1};   // virtual completion times of the units when it was picked
 };
 
 // Search state of one unit: measured candidates (default first), the queue
@@ -219,7 +227,13 @@ class Tuner {
 
   private:
     bool expired() const { return Clock::now() >= deadline_; }
-    int rows_of(int unit) const { return (unit ? w_ : 1) * g_; }
+    int rows_of(int unit) const { return (unit == 1 ? w_ : 1) * g_; }
+    q8k4v_config unit_default(int unit) const {
+        return unit == 2 ? cascade_default_config(g_) : default_config(rows_of(unit));
+    }
+    const char* unit_name(int unit) const { return unit == 0 ? "decode" : unit == 1 ? "verify" : "multi_session"; }
+    int cascade_shape(Shape* s, const std::string& name, int ctx, bool small, std::vector<int32_t>* lens,
+                      std::vector<int32_t>* rows) const;
     int32_t setup(std::string* why);
     int32_t launch(const q8k4v_config* cfg, const Shape& s, int copy, int set, float* out, const void* q);
     int32_t time_shape(const q8k4v_config* cfg, const Shape& s, double* median_us);
@@ -236,24 +250,28 @@ class Tuner {
     Arena arena_;
     hipStream_t stream_ = nullptr;
     std::vector<hipEvent_t> events_;
-    int hq_ = 0, h_ = 0, d_ = 0, w_ = 0, g_ = 0;
+    int hq_ = 0, h_ = 0, d_ = 0, w_ = 0, g_ = 0, n_units_ = 2, ns_ = 0;
     float scale_ = 0;
     int pages_ = 0, small_pages_ = 0, n_copies_ = 0, n_sets_ = 0, reps_ = 0;
+    int casc_window_ = 0, n_csets_ = 0;  // multi-session small shape: pages per set, sets
+    double llc_multiple_ = 0;            // least bytes streamed per replay over the shapes, / LLC
     size_t cache_bytes_ = 0;
     std::vector<q8k4v_cache> copies_;
     int32_t* d_tables_ = nullptr;        // [n_sets][pages]: set 0 is the full permutation
     int32_t* d_lens_ = nullptr;          // [4]: decode small, decode large, verify small, verify large
-    int32_t* d_ref_lens_ = nullptr;      // [4]: the caller's reference lengths per term
-    void* d_q_ = nullptr;                // bf16 [w][hq][d]
-    float* d_out_ = nullptr;             // fp32 [w][hq][d]
+    int32_t* d_ref_lens_ = nullptr;      // [4]: the caller's reference lengths of the decode / verify terms
+    int32_t* d_casc_tables_ = nullptr;   // cascade page tables: [n_csets][ns][small max_pages], then [ns][large max_pages]
+    int32_t* d_casc_lens_ = nullptr;     // cascade session lengths: [ns] small, [ns] large
+    void* d_q_ = nullptr;                // bf16 [max(w, ns)][hq][d]
+    float* d_out_ = nullptr;             // fp32 [max(w, ns)][hq][d]
     void* d_ws_ = nullptr;
     size_t ws_bytes_ = 0;
-    Shape shapes_[2][2];                 // [unit][small/large]
-    std::vector<float> def_out_[2][2];   // default outputs per unit/shape on copy 0
-    double noise_[2][2] = {{0, 0}, {0, 0}};
-    double def_t_[2][2] = {{0, 0}, {0, 0}};
+    Shape shapes_[kUnits][2];            // [unit][small/large]
+    std::vector<float> def_out_[kUnits][2];   // default outputs per unit/shape on copy 0
+    double noise_[kUnits][2] = {{0, 0}, {0, 0}, {0, 0}};
+    double def_t_[kUnits][2] = {{0, 0}, {0, 0}, {0, 0}};
     std::string setup_note_;
-    int seq_ = 0;                        // measurement order over both units
+    int seq_ = 0;                        // measurement order over all units
     std::string summary_, error_;
 
   public:
@@ -261,25 +279,79 @@ class Tuner {
     const std::string& error() const { return error_; }
 };
 
+// A multi-session shape at context ctx: ns sessions share a ctx / 2 token
+// prefix (whole pages); session i owns a private suffix of about
+// (i + 1) / ns x ctx / 2 tokens (whole pages less i % 16 tokens: ragged
+// lengths, a ragged last page), so the suffixes average about ctx / 4 tokens
+// and the shortest and longest differ by ns.  The sessions' pages are
+// window-relative: the prefix first, then each suffix in turn.  `rows` gets
+// each session's page indices (max_pages each); returns the window's pages.
+int Tuner::cascade_shape(Shape* s, const std::string& name, int ctx, bool small, std::vector<int32_t>* lens,
+                         std::vector<int32_t>* rows) const {
+    const int pre = std::max(1, ctx / 2 / Q8K4V_PAGE_SIZE);
+    const int most = std::max(1, ctx / 2 / Q8K4V_PAGE_SIZE);    // the longest suffix, in pages
+    s->name = name;
+    s->kind = 2;
+    s->n_draft = 1;
+    s->small = small;
+    s->n_seqs = ns_;
+    s->n_pref = pre;
+    s->max_pages = pre + most;
+    lens->assign(ns_, 0);
+    rows->assign((size_t)ns_ * s->max_pages, 0);
+    int longest = 0, next = pre;
+    for (int i = 0; i < ns_; ++i) {
+        const int own = std::max(1, (int)((int64_t)most * (i + 1) / ns_));
+        (*lens)[i] = Q8K4V_PAGE_SIZE * (pre + own) - i % 16;
+        longest = std::max(longest, (*lens)[i]);
+        for (int j = 0; j < s->max_pages; ++j)
+            (*rows)[(size_t)i * s->max_pages + j] = j < pre ? j : j < pre + own ? next + (j - pre) : 0;
+        next += own;
+    }
+    s->ctx = longest;
+    return next;
+}
+
 int32_t Tuner::setup(std::string* why) {
     hq_ = req_.num_q_heads;
     h_ = req_.num_kv_heads;
     d_ = req_.head_dim;
     w_ = req_.n_draft;
     g_ = hq_ / h_;
+    ns_ = req_.n_sessions >= 2 ? req_.n_sessions : 0;
+    n_units_ = ns_ ? 3 : 2;
     scale_ = req_.softmax_scale > 0 ? req_.softmax_scale : 1.0f / std::sqrt((float)d_);
     const int ctx_s = req_.ctx_small, ctx_l = req_.ctx_large;
-    pages_ = (ctx_l + w_ + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE;
+    const int dv_pages = (ctx_l + w_ + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE;
     small_pages_ = (ctx_s + w_ + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE;
-    n_sets_ = std::max(1, pages_ / small_pages_);
-    const size_t per_th = (size_t)d_ + 2 + d_ / 2 + 2 * (d_ / 32);
-    cache_bytes_ = (size_t)pages_ * h_ * Q8K4V_PAGE_SIZE * per_th;
-    const int want = std::max(2, (int)((4 * kLlcBytes + cache_bytes_ - 1) / cache_bytes_) + 1);
 
-    shapes_[0][0] = {"decode@" + std::to_string(ctx_s), 1, ctx_s, true};
-    shapes_[0][1] = {"decode@" + std::to_string(ctx_l), 1, ctx_l, false};
-    shapes_[1][0] = {"verify@" + std::to_string(ctx_s) + "+" + std::to_string(w_), w_, ctx_s + w_, true};
-    shapes_[1][1] = {"verify@" + std::to_string(ctx_l) + "+" + std::to_string(w_), w_, ctx_l + w_, false};
+    shapes_[0][0] = {"decode@" + std::to_string(ctx_s), 0, 1, ctx_s, true};
+    shapes_[0][1] = {"decode@" + std::to_string(ctx_l), 0, 1, ctx_l, false};
+    shapes_[1][0] = {"verify@" + std::to_string(ctx_s) + "+" + std::to_string(w_), 1, w_, ctx_s + w_, true};
+    shapes_[1][1] = {"verify@" + std::to_string(ctx_l) + "+" + std::to_string(w_), 1, w_, ctx_l + w_, false};
+    std::vector<int32_t> lens_s, rows_s, lens_l, rows_l;
+    int casc_large_window = 0;
+    if (ns_) {
+        casc_window_ = cascade_shape(&shapes_[2][0], std::to_string(ns_) + " sessions@" + std::to_string(ctx_s / 2) +
+                                     " shared", ctx_s, true, &lens_s, &rows_s);
+        casc_large_window = cascade_shape(&shapes_[2][1], std::to_string(ns_) + " sessions@" +
+                                          std::to_string(ctx_l / 2) + " shared", ctx_l, false, &lens_l, &rows_l);
+    }
+    // the pool of every copy: the large decode / verify context, or the large
+    // multi-session window if that is larger
+    pages_ = std::max(dv_pages, casc_large_window);
+    const size_t per_th = (size_t)d_ + 2 + d_ / 2 + 2 * (d_ / 32);
+    const size_t page_bytes = (size_t)h_ * Q8K4V_PAGE_SIZE * per_th;
+    cache_bytes_ = (size_t)pages_ * page_bytes;
+    // enough copies that every shape's replay streams 4x the LLC before a
+    // copy comes round again: per copy, a large shape reads its pages, a
+    // small one at most its disjoint page sets
+    const size_t dv_bytes = (size_t)dv_pages * page_bytes;
+    size_t per_copy = std::min(dv_bytes, (size_t)(pages_ / small_pages_) * small_pages_ * page_bytes);
+    if (ns_)
+        per_copy = std::min({per_copy, (size_t)casc_large_window * page_bytes,
+                             (size_t)(pages_ / casc_window_) * casc_window_ * page_bytes});
+    const int want = std::max(2, (int)((4 * kLlcBytes + per_copy - 1) / per_copy) + 1);
 
     // workspace: the largest any candidate can ask for (split count is capped
     // by the combine, so the bound is the cap times the row records)
@@ -287,25 +359,49 @@ int32_t Tuner::setup(std::string* why) {
     int max_len = ctx_l + w_;
     for (int k = 0; k < 4; ++k)
         if (has_ref(k)) max_len = std::max(max_len, req_.ref[k].len);
-    for (int unit = 0; unit < 2; ++unit)
-        for (int wgs : {1, 2, 3, 4, 6})
+    for (int unit = 0; unit < n_units_; ++unit)
+        for (int wgs : {1, 2, 3, 4, 6, 8})
             for (int waves : {2, 4, 8})
                 for (int variant : {0, 4, 5}) {
-                    q8k4v_config c = default_config(rows_of(unit));
+                    q8k4v_config c = unit_default(unit);
                     c.wgs_per_cu = wgs;
                     c.waves_per_wg = waves;
                     c.variant = variant;
                     c.stages = 0;
-                    c.fused_combine = 1;
-                    const int nd = unit ? w_ : 1;
-                    ws_bytes_ = std::max(ws_bytes_, q8k4v_workspace_bytes(1, hq_, h_, d_, max_len, nd, &c));
+                    c.fused_combine = unit == 2 ? 0 : 1;
+                    if (unit < 2) {
+                        ws_bytes_ = std::max(ws_bytes_, q8k4v_workspace_bytes(1, hq_, h_, d_, max_len, unit ? w_ : 1, &c));
+                        continue;
+                    }
+                    for (int k = 0; k < 2; ++k) {
+                        const Shape& sh = shapes_[2][k];
+                        ws_bytes_ = std::max(ws_bytes_, q8k4v_prefix_workspace_bytes(ns_, hq_, h_, d_, sh.ctx, sh.n_pref, &c));
+                        const q8k4v_tune_ref& r = req_.ref[4 + k];
+                        if (r.cache)
+                            ws_bytes_ = std::max(ws_bytes_, q8k4v_prefix_workspace_bytes(r.n_seqs, hq_, h_, d_, r.len,
+                                                                                         r.n_prefix_pages, &c));
+                    }
                 }
     ws_bytes_ = std::max<size_t>(ws_bytes_, Q8K4V_WS_HEADER_BYTES);
+    int qrows = std::max(w_, ns_);
+    for (int k = 4; k < 6; ++k)
+        if (ns_ && has_ref(k)) qrows = std::max(qrows, req_.ref[k].n_seqs);
+    // page sets of the small shapes: disjoint windows of the pool, as many as
+    // make a replay stream 4x the LLC over the copies (at most what fits); the
+    // memory admission below assumes the most
+    auto sets_for = [&](int window, int copies) {
+        const size_t per = (size_t)copies * window * page_bytes;
+        return std::max(1, std::min(pages_ / window, (int)((4 * kLlcBytes + per - 1) / per) + 1));
+    };
+    const int most_csets = ns_ ? std::max(1, pages_ / casc_window_) : 0;
+    const size_t casc_table_ints = ns_ ? (size_t)most_csets * rows_s.size() + rows_l.size() : 0;
+    n_sets_ = std::max(1, pages_ / small_pages_);
 
     size_t free_b = 0, total_b = 0;
     if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: hipMemGetInfo");
     const size_t cap = req_.mem_cap_bytes ? std::min(req_.mem_cap_bytes, free_b) : free_b;
-    const size_t fixed = ws_bytes_ + (size_t)n_sets_ * pages_ * 4 + (size_t)w_ * hq_ * d_ * 6 + (64u << 20);
+    const size_t fixed = ws_bytes_ + (size_t)n_sets_ * pages_ * 4 + casc_table_ints * 4 + (size_t)qrows * hq_ * d_ * 6 +
+                         (64u << 20);
     int copies = want;
     while (copies >= 2 && fixed + (size_t)copies * cache_bytes_ > cap) --copies;
     if (copies < 2) {
@@ -315,6 +411,15 @@ int32_t Tuner::setup(std::string* why) {
     }
     if (copies < want) setup_note_ = "rotation limited by memory: " + std::to_string(copies) + " of " + std::to_string(want) + " copies";
     n_copies_ = copies;
+    n_sets_ = sets_for(small_pages_, n_copies_);
+    n_csets_ = ns_ ? sets_for(casc_window_, n_copies_) : 0;
+    // bytes streamed by one replay of each shape's graph, over the LLC
+    llc_multiple_ = (double)n_copies_ * n_sets_ * small_pages_ * page_bytes / (double)kLlcBytes;
+    llc_multiple_ = std::min(llc_multiple_, (double)n_copies_ * dv_bytes / (double)kLlcBytes);
+    if (ns_) {
+        llc_multiple_ = std::min(llc_multiple_, (double)n_copies_ * n_csets_ * casc_window_ * page_bytes / (double)kLlcBytes);
+        llc_multiple_ = std::min(llc_multiple_, (double)n_copies_ * casc_large_window * page_bytes / (double)kLlcBytes);
+    }
 
     if (hipStreamCreateWithFlags(&stream_, hipStreamNonBlocking) != hipSuccess)
         return hip_fail(hipGetLastError(), "tune_select: stream");
@@ -360,13 +465,25 @@ int32_t Tuner::setup(std::string* why) {
     for (int set = 0; set < n_sets_; ++set)
         for (int i = 0; i < pages_; ++i)
             tables[(size_t)set * pages_ + i] = perm[(i + (size_t)set * small_pages_) % pages_];
+    // cascade tables: the window-relative pages through the same permutation
+    // (small shape: set j's window starts at page j * window; large shape: at 0)
+    std::vector<int32_t> casc_tables(ns_ ? (size_t)n_csets_ * rows_s.size() + rows_l.size() : 0);
+    if (ns_) {
+        for (int set = 0; set < n_csets_; ++set)
+            for (size_t i = 0; i < rows_s.size(); ++i)
+                casc_tables[set * rows_s.size() + i] = perm[(rows_s[i] + (size_t)set * casc_window_) % pages_];
+        for (size_t i = 0; i < rows_l.size(); ++i) casc_tables[n_csets_ * rows_s.size() + i] = perm[rows_l[i]];
+    }
     d_tables_ = (int32_t*)arena_.alloc(tables.size() * 4);
     d_lens_ = (int32_t*)arena_.alloc(16);
     d_ref_lens_ = (int32_t*)arena_.alloc(16);
-    d_q_ = arena_.alloc((size_t)w_ * hq_ * d_ * 2);
-    d_out_ = (float*)arena_.alloc((size_t)w_ * hq_ * d_ * 4);
+    d_casc_tables_ = ns_ ? (int32_t*)arena_.alloc(casc_tables.size() * 4) : nullptr;
+    d_casc_lens_ = ns_ ? (int32_t*)arena_.alloc((size_t)2 * ns_ * 4) : nullptr;
+    d_q_ = arena_.alloc((size_t)qrows * hq_ * d_ * 2);
+    d_out_ = (float*)arena_.alloc((size_t)qrows * hq_ * d_ * 4);
     d_ws_ = arena_.alloc(ws_bytes_);
-    if (!d_tables_ || !d_lens_ || !d_ref_lens_ || !d_q_ || !d_out_ || !d_ws_) {
+    if (!d_tables_ || !d_lens_ || !d_ref_lens_ || !d_q_ || !d_out_ || !d_ws_ ||
+        (ns_ && (!d_casc_tables_ || !d_casc_lens_))) {
         *why = "hipMalloc failed";
         return Q8K4V_ENOMEM;
     }
@@ -376,7 +493,17 @@ int32_t Tuner::setup(std::string* why) {
         hipMemcpyAsync(d_lens_, lens, sizeof lens, hipMemcpyHostToDevice, stream_) != hipSuccess ||
         hipMemcpyAsync(d_ref_lens_, ref_lens, sizeof ref_lens, hipMemcpyHostToDevice, stream_) != hipSuccess)
         return hip_fail(hipGetLastError(), "tune_select: upload");
-    hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream_, (uint16_t*)d_q_, (size_t)w_ * hq_ * d_,
+    if (ns_) {
+        std::vector<int32_t> cl(lens_s);
+        cl.insert(cl.end(), lens_l.begin(), lens_l.end());
+        if (hipMemcpyAsync(d_casc_tables_, casc_tables.data(), casc_tables.size() * 4, hipMemcpyHostToDevice, stream_) !=
+                hipSuccess ||
+            hipMemcpyAsync(d_casc_lens_, cl.data(), cl.size() * 4, hipMemcpyHostToDevice, stream_) != hipSuccess)
+            return hip_fail(hipGetLastError(), "tune_select: upload");
+        // the host vectors must outlive the copies
+        if (hipStreamSynchronize(stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: upload");
+    }
+    hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream_, (uint16_t*)d_q_, (size_t)qrows * hq_ * d_,
                        req_.seed ^ 0xA11CEULL);
     // the workspace header (the in-launch merge's counters) starts at zero;
     // every completed launch leaves it at zero, whatever its plan
@@ -391,9 +518,16 @@ int32_t Tuner::setup(std::string* why) {
 }
 
 int32_t Tuner::launch(const q8k4v_config* cfg, const Shape& s, int copy, int set, float* out, const void* q) {
-    const int32_t* lens = d_lens_ + (s.n_draft > 1 ? 2 : 0) + (s.small ? 0 : 1);
+    if (s.kind == 2) {      // sessions over the shared prefix (small shape: page set `set`)
+        const size_t small_rows = (size_t)ns_ * shapes_[2][0].max_pages;
+        const int32_t* table = d_casc_tables_ + (s.small ? (size_t)set * small_rows : (size_t)n_csets_ * small_rows);
+        const int32_t* lens = d_casc_lens_ + (s.small ? 0 : ns_);
+        return attn_decode_prefix_q8k4v(&copies_[copy], q, Q8K4V_BF16, out, ns_, hq_, lens, s.ctx, table, s.max_pages,
+                                        s.n_pref, scale_, cfg, d_ws_, ws_bytes_, stream_);
+    }
+    const int32_t* lens = d_lens_ + (s.kind == 1 ? 2 : 0) + (s.small ? 0 : 1);
     const int32_t* table = d_tables_ + (size_t)(s.small ? set : 0) * pages_;
-    if (s.n_draft > 1)
+    if (s.kind == 1)
         return attn_verify_q8k4v(&copies_[copy], q, Q8K4V_BF16, out, 1, hq_, s.n_draft, lens, s.ctx, table, pages_,
                                  scale_, cfg, d_ws_, ws_bytes_, stream_);
     return attn_decode_q8k4v(&copies_[copy], q, Q8K4V_BF16, out, 1, hq_, lens, s.ctx, table, pages_, scale_, cfg,
@@ -408,13 +542,14 @@ int32_t Tuner::time_shape(const q8k4v_config* cfg, const Shape& s, double* media
     // serving loop issues these launches (no host launch gap between them);
     // the time per launch is a replay's time over its launches, the median
     // over reps_ timed replays after one untimed.
-    const int G = s.small ? n_copies_ * n_sets_ : n_copies_;
+    const int sets = s.kind == 2 ? n_csets_ : n_sets_;
+    const int G = s.small ? n_copies_ * sets : n_copies_;
     hipGraph_t graph = nullptr;
     if (hipStreamBeginCapture(stream_, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return hip_fail(hipGetLastError(), "tune_select: begin capture");
     int32_t rc = Q8K4V_OK;
     for (int r = 0; r < G && rc == Q8K4V_OK; ++r)
-        rc = launch(cfg, s, r % n_copies_, s.small ? (r / n_copies_) % n_sets_ : 0, d_out_, d_q_);
+        rc = launch(cfg, s, r % n_copies_, s.small ? (r / n_copies_) % sets : 0, d_out_, d_q_);
     const hipError_t ec = hipStreamEndCapture(stream_, &graph);
     if (rc != Q8K4V_OK || ec != hipSuccess) {
         if (graph) (void)hipGraphDestroy(graph);
@@ -446,7 +581,7 @@ int32_t Tuner::time_shape(const q8k4v_config* cfg, const Shape& s, double* media
 }
 
 int32_t Tuner::output(const q8k4v_config* cfg, const Shape& s, int copy, std::vector<float>* host) {
-    const size_t n = (size_t)s.n_draft * hq_ * d_;
+    const size_t n = (size_t)(s.kind == 2 ? ns_ : s.n_draft) * hq_ * d_;
     if (hipMemsetAsync(d_out_, 0xFF, n * 4, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
     const int32_t rc = launch(cfg, s, copy, 0, d_out_, d_q_);
     if (rc != Q8K4V_OK) return rc;
@@ -457,16 +592,19 @@ int32_t Tuner::output(const q8k4v_config* cfg, const Shape& s, int copy, std::ve
     return Q8K4V_OK;
 }
 
-// Output of a candidate on reference term `term` (0, 1 decode; 2, 3 verify).
+// Output of a candidate on reference term `term` (0, 1 decode; 2, 3 verify;
+// 4, 5 sessions over a shared prefix).
 int32_t Tuner::ref_output(const q8k4v_config* cfg, int term, std::vector<float>* host) {
     const q8k4v_tune_ref& r = req_.ref[term];
-    const bool verify = term >= 2;
-    const int nd = verify ? w_ : 1;
-    const size_t n = (size_t)nd * hq_ * d_;
+    const int nrows = term >= 4 ? r.n_seqs : term >= 2 ? w_ : 1;
+    const size_t n = (size_t)nrows * hq_ * d_;
     int32_t rc;
     if (hipMemsetAsync(d_out_, 0xFF, n * 4, stream_) != hipSuccess) return hip_fail(hipGetLastError(), "tune_select: memset");
-    if (verify)
-        rc = attn_verify_q8k4v(r.cache, r.q, Q8K4V_BF16, d_out_, 1, hq_, nd, d_ref_lens_ + term, r.len, r.page_table,
+    if (term >= 4)
+        rc = attn_decode_prefix_q8k4v(r.cache, r.q, Q8K4V_BF16, d_out_, r.n_seqs, hq_, r.seq_lens, r.len, r.page_table,
+                                      r.max_pages, r.n_prefix_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
+    else if (term >= 2)
+        rc = attn_verify_q8k4v(r.cache, r.q, Q8K4V_BF16, d_out_, 1, hq_, w_, d_ref_lens_ + term, r.len, r.page_table,
                                r.max_pages, scale_, cfg, d_ws_, ws_bytes_, stream_);
     else
         rc = attn_decode_q8k4v(r.cache, r.q, Q8K4V_BF16, d_out_, 1, hq_, d_ref_lens_ + term, r.len, r.page_table,
@@ -551,7 +689,7 @@ void Tuner::measure(int unit, Cand* c) {
 void Tuner::start_unit(int unit, UnitSearch* u) {
     const int rows = rows_of(unit);
     const bool paged16 = rows == 1 || rows == 2 || rows == 4 || rows == 8 || rows == 16;
-    const q8k4v_config dflt = default_config(rows);
+    const q8k4v_config dflt = unit_default(unit);
     const auto t0 = Clock::now();
     Cand d;
     d.cfg = dflt;
@@ -601,7 +739,8 @@ void Tuner::start_unit(int unit, UnitSearch* u) {
         Cand c;
         c.cfg = dflt;
         c.cfg.variant = v;
-        c.cfg.wgs_per_cu = c.cfg.waves_per_wg = c.cfg.stages = 0;
+        c.cfg.waves_per_wg = c.cfg.stages = 0;
+        if (unit != 2) c.cfg.wgs_per_cu = 0;     // the cascade's suffix keeps its finer default split
         c.stage = "structural";
         u->queue.push_back(c);
     }
@@ -622,11 +761,15 @@ void Tuner::refine_queue(int unit, UnitSearch* u) {
         ++u->generated;
     };
     // launch shapes both kernels accept: 2, 4 or 8 waves, 2 or 3 stages; one
-    // 8-wave workgroup fills a CU's LDS, so 8 waves take one or two per CU
+    // 8-wave workgroup fills a CU's LDS, so 8 waves take one or two per CU.
+    // The cascade's suffix pass (unit 2) merges in the cascade's own combine
+    // (no in-launch merge) and takes finer splits over ragged sessions.
     for (int fused : {0, 1})
         for (int stages : {2, 3})
             for (int waves : {4, 8, 2})
-                for (int wgs : {1, 2, 3, 4, 6}) {
+                for (int wgs : {1, 2, 3, 4, 6, 8}) {
+                    if (unit == 2 && fused) continue;
+                    if (unit != 2 && wgs == 8) continue;
                     if (waves == 8 && wgs > 2) continue;
                     if (!base_paged && waves == 2 && wgs > 4) continue;
                     q8k4v_config c = base;
@@ -669,39 +812,40 @@ std::string identity_hash(const std::string& id) {   // FNV-1a, 64 bits
 
 constexpr const char* kRecordTag = "q8k4v-tune-record";
 
-// One stored choice: identity hash, request shape, unit, qualified flag and
-// the configuration, then a tab and the identity in words.
+// One stored choice: identity hash, request shape (with the session count
+// of the multi-session unit), unit, qualified flag and the configuration, then
+// a tab and the identity in words.
 struct Record {
     std::string id_hash;
-    int n_draft = 0, hq = 0, hkv = 0, d = 0, ctx_small = 0, ctx_large = 0, unit = 0, qualified = 0;
+    int n_draft = 0, hq = 0, hkv = 0, d = 0, ctx_small = 0, ctx_large = 0, n_sessions = 0, unit = 0, qualified = 0;
     q8k4v_config cfg{};
 };
 
 std::string record_line(const Record& r, const std::string& identity) {
     char b[512];
-    std::snprintf(b, sizeof b, "%s 1 %s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d\t%s", kRecordTag,
-                  r.id_hash.c_str(), r.n_draft, r.hq, r.hkv, r.d, r.ctx_small, r.ctx_large, r.unit, r.qualified,
-                  r.cfg.variant, r.cfg.wgs_per_cu, r.cfg.split_pages, r.cfg.tile_pages, r.cfg.waves_per_wg,
-                  r.cfg.fused_combine, r.cfg.stages, identity.c_str());
+    std::snprintf(b, sizeof b, "%s 2 %s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d\t%s", kRecordTag,
+                  r.id_hash.c_str(), r.n_draft, r.hq, r.hkv, r.d, r.ctx_small, r.ctx_large, r.n_sessions, r.unit,
+                  r.qualified, r.cfg.variant, r.cfg.wgs_per_cu, r.cfg.split_pages, r.cfg.tile_pages,
+                  r.cfg.waves_per_wg, r.cfg.fused_combine, r.cfg.stages, identity.c_str());
     return b;
 }
 
 bool parse_record(const std::string& line, Record* r) {
     char tag[32] = {0}, hash[32] = {0};
     int ver = 0;
-    int v[15];
-    const int n = std::sscanf(line.c_str(), "%31s %d %31s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", tag, &ver,
+    int v[16];
+    const int n = std::sscanf(line.c_str(), "%31s %d %31s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d", tag, &ver,
                               hash, &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &v[7], &v[8], &v[9], &v[10],
-                              &v[11], &v[12], &v[13], &v[14]);
-    if (n != 18 || std::strcmp(tag, kRecordTag) != 0 || ver != 1 || std::strlen(hash) != 16) return false;
+                              &v[11], &v[12], &v[13], &v[14], &v[15]);
+    if (n != 19 || std::strcmp(tag, kRecordTag) != 0 || ver != 2 || std::strlen(hash) != 16) return false;
     r->id_hash = hash;
     r->n_draft = v[0]; r->hq = v[1]; r->hkv = v[2]; r->d = v[3]; r->ctx_small = v[4]; r->ctx_large = v[5];
-    r->unit = v[6]; r->qualified = v[7];
+    r->n_sessions = v[6]; r->unit = v[7]; r->qualified = v[8];
     std::memset(&r->cfg, 0, sizeof r->cfg);
-    r->cfg.variant = v[8]; r->cfg.wgs_per_cu = v[9]; r->cfg.split_pages = v[10]; r->cfg.tile_pages = v[11];
-    r->cfg.waves_per_wg = v[12]; r->cfg.fused_combine = v[13]; r->cfg.stages = v[14];
+    r->cfg.variant = v[9]; r->cfg.wgs_per_cu = v[10]; r->cfg.split_pages = v[11]; r->cfg.tile_pages = v[12];
+    r->cfg.waves_per_wg = v[13]; r->cfg.fused_combine = v[14]; r->cfg.stages = v[15];
     r->cfg.qualified = r->qualified;
-    return r->unit == 0 || r->unit == 1;
+    return r->unit >= 0 && r->unit < kUnits;
 }
 
 std::vector<std::string> read_lines(const char* path) {
@@ -717,8 +861,9 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     std::string why;
     g_ = req_.num_q_heads / req_.num_kv_heads;
     w_ = req_.n_draft;
-    out_table[0] = default_config(rows_of(0));
-    out_table[1] = default_config(rows_of(1));
+    ns_ = req_.n_sessions >= 2 ? req_.n_sessions : 0;
+    n_units_ = ns_ ? 3 : 2;
+    for (int unit = 0; unit < n_units_; ++unit) out_table[unit] = unit_default(unit);
     // stored choice for this device identity and request shape
     const std::string identity = device_identity();
     const std::string id_hash = identity_hash(identity);
@@ -726,29 +871,30 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     auto matches = [&](const Record& r) {
         return r.id_hash == id_hash && r.n_draft == req_.n_draft && r.hq == req_.num_q_heads &&
                r.hkv == req_.num_kv_heads && r.d == req_.head_dim && r.ctx_small == req_.ctx_small &&
-               r.ctx_large == req_.ctx_large;
+               r.ctx_large == req_.ctx_large && r.n_sessions == ns_;
     };
     std::string record_action = "none";
-    bool stored[2] = {false, false};
-    Record rec[2];
+    bool stored[kUnits] = {false, false, false};
+    Record rec[kUnits];
     if (use_records) {
         for (const auto& line : read_lines(req_.record_path)) {
             Record r;
-            if (parse_record(line, &r) && matches(r)) {
+            if (parse_record(line, &r) && matches(r) && r.unit < n_units_) {
                 rec[r.unit] = r;
                 stored[r.unit] = true;
             }
         }
     }
-    const bool from_records = stored[0] && stored[1];
-    std::vector<Cand> cands[2];
-    q8k4v_config chosen[2] = {out_table[0], out_table[1]};
-    bool qual[2] = {false, false};
+    bool from_records = true;
+    for (int unit = 0; unit < n_units_; ++unit) from_records = from_records && stored[unit];
+    std::vector<Cand> cands[kUnits];
+    q8k4v_config chosen[kUnits] = {out_table[0], out_table[1], out_table[n_units_ - 1]};
+    bool qual[kUnits] = {false, false, false};
     bool searched = false;
     int32_t rc = Q8K4V_OK;
     if (from_records) {
         record_action = "loaded";
-        for (int unit = 0; unit < 2; ++unit) {
+        for (int unit = 0; unit < n_units_; ++unit) {
             chosen[unit] = rec[unit].cfg;
             qual[unit] = rec[unit].qualified != 0;
         }
@@ -757,19 +903,19 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     }
     if (!from_records && rc == Q8K4V_OK && !expired()) {
         searched = true;
-        UnitSearch us[2];
-        for (int unit = 0; unit < 2; ++unit) start_unit(unit, &us[unit]);
+        UnitSearch us[kUnits];
+        for (int unit = 0; unit < n_units_; ++unit) start_unit(unit, &us[unit]);
         const int limit = req_.max_candidates > 0 ? req_.max_candidates : (1 << 20);
         for (;;) {
             // the next candidate comes from the unit with the earliest virtual
             // completion time; a unit whose structural variants are done gets
             // its refinement queue first
             double share_den = 0;
-            for (int unit = 0; unit < 2; ++unit)
+            for (int unit = 0; unit < n_units_; ++unit)
                 if (us[unit].active) share_den += def_t_[unit][0] + def_t_[unit][1];
-            double vt[2] = {-1, -1};
+            double vt[kUnits] = {-1, -1, -1};
             int pick = -1;
-            for (int unit = 0; unit < 2; ++unit) {
+            for (int unit = 0; unit < n_units_; ++unit) {
                 UnitSearch& u = us[unit];
                 if (!u.active || (int)u.cands.size() >= limit) continue;
                 if (u.queue.empty() && !u.refined) refine_queue(unit, &u);
@@ -790,8 +936,7 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             Cand x = u.queue.front();
             u.queue.erase(u.queue.begin());
             x.seq = seq_++;
-            x.vt[0] = vt[0];
-            x.vt[1] = vt[1];
+            for (int unit = 0; unit < kUnits; ++unit) x.vt[unit] = vt[unit];
             const auto t0c = Clock::now();
             measure(pick, &x);
             const double dt = std::chrono::duration<double, std::milli>(Clock::now() - t0c).count();
@@ -800,7 +945,7 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             u.cands.push_back(x);
             if (x.verdict == "admitted" && x.cost < u.cands[u.best_i].cost) u.best_i = u.cands.size() - 1;
             if (x.verdict == "unknown") {   // the deadline passed: the rest stays unmeasured
-                for (int unit = 0; unit < 2; ++unit)
+                for (int unit = 0; unit < n_units_; ++unit)
                     for (auto& q : us[unit].queue) {
                         q.verdict = "unknown";
                         q.why = "deadline";
@@ -809,7 +954,7 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
                 break;
             }
         }
-        for (int unit = 0; unit < 2; ++unit) {
+        for (int unit = 0; unit < n_units_; ++unit) {
             cands[unit] = us[unit].cands;
             if (us[unit].cands.empty()) continue;
             const Cand& b = us[unit].cands[us[unit].best_i];
@@ -817,20 +962,20 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             qual[unit] = b.verdict == "admitted";
         }
     }
-    for (int unit = 0; unit < 2; ++unit) {
+    for (int unit = 0; unit < n_units_; ++unit) {
         out_table[unit] = chosen[unit];
         out_table[unit].qualified = qual[unit] ? 1 : 0;
         if (!qual[unit]) {
-            out_table[unit] = default_config(rows_of(unit));
+            out_table[unit] = unit_default(unit);
             out_table[unit].qualified = 0;
         }
     }
     bool install = false;
     if (req_.install && rc == Q8K4V_OK)
-        for (int unit = 0; unit < 2; ++unit)
+        for (int unit = 0; unit < n_units_; ++unit)
             if (qual[unit]) {
-                tuned_install(unit ? req_.n_draft : 1, req_.num_q_heads, req_.num_kv_heads, req_.head_dim,
-                              out_table[unit]);
+                const int key = unit == 0 ? 1 : unit == 1 ? req_.n_draft : kTunedCascadeKey;
+                tuned_install(key, req_.num_q_heads, req_.num_kv_heads, req_.head_dim, out_table[unit]);
                 install = true;
             }
     // store a completed search (records of other identities and shapes stay)
@@ -840,11 +985,11 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             Record r;
             if (parse_record(line, &r) && !matches(r)) keep.push_back(line);
         }
-        for (int unit = 0; unit < 2; ++unit) {
+        for (int unit = 0; unit < n_units_; ++unit) {
             Record r;
             r.id_hash = id_hash;
             r.n_draft = req_.n_draft; r.hq = req_.num_q_heads; r.hkv = req_.num_kv_heads; r.d = req_.head_dim;
-            r.ctx_small = req_.ctx_small; r.ctx_large = req_.ctx_large;
+            r.ctx_small = req_.ctx_small; r.ctx_large = req_.ctx_large; r.n_sessions = ns_;
             r.unit = unit;
             r.qualified = qual[unit] ? 1 : 0;
             r.cfg = out_table[unit];
@@ -869,16 +1014,18 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
     j += ",\"alpha\":" + fmt(kAlpha);
     if (!why.empty()) j += ",\"error\":\"" + why + "\"";
     j += ",\"rotation\":{\"copies\":" + std::to_string(n_copies_) + ",\"copy_bytes\":" + std::to_string(cache_bytes_) +
-         ",\"small_page_sets\":" + std::to_string(n_sets_) + ",\"llc_multiple\":" +
-         fmt((double)n_copies_ * cache_bytes_ / (double)kLlcBytes) + ",\"timed_replays\":" + std::to_string(reps_) + ",\"launches_per_replay\":[" +
-         std::to_string(n_copies_ * n_sets_) + "," + std::to_string(n_copies_) + "]}";
+         ",\"small_page_sets\":" + std::to_string(n_sets_) + ",\"session_page_sets\":" + std::to_string(n_csets_) +
+         ",\"llc_multiple\":" + fmt(llc_multiple_) + ",\"timed_replays\":" + std::to_string(reps_) +
+         ",\"launches_per_replay\":[" + std::to_string(n_copies_ * n_sets_) + "," + std::to_string(n_copies_);
+    if (ns_) j += "," + std::to_string(n_copies_ * n_csets_) + "," + std::to_string(n_copies_);
+    j += "]}";
     if (!setup_note_.empty()) j += ",\"note\":\"" + setup_note_ + "\"";
     j += ",\"installed\":" + std::string(install ? "true" : "false");
     j += ",\"identity\":\"" + identity + "\",\"identity_hash\":\"" + id_hash + "\"";
     j += ",\"record\":\"" + record_action + "\"";
     j += ",\"units\":[";
     std::string cand_lists;
-    for (int unit = 0; unit < 2; ++unit) {
+    for (int unit = 0; unit < n_units_; ++unit) {
         if (unit) j += ",";
         int n_adm = 0, n_rej = 0, n_unk = 0, n_inv = 0, n_alpha = 0, n_oracle = 0;
         std::vector<std::string> invalid_why;
@@ -892,8 +1039,9 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             if (c.verdict == "invalid" && std::find(invalid_why.begin(), invalid_why.end(), c.why) == invalid_why.end())
                 invalid_why.push_back(c.why);
         }
-        j += "{\"unit\":\"" + std::string(unit ? "verify" : "decode") + "\"";
-        j += ",\"rows_per_kv_head\":" + std::to_string((unit ? w_ : 1) * g_);
+        j += "{\"unit\":\"" + std::string(unit_name(unit)) + "\"";
+        j += ",\"rows_per_kv_head\":" + std::to_string(rows_of(unit));
+        if (unit == 2) j += ",\"sessions\":" + std::to_string(ns_);
         j += ",\"shapes\":[\"" + shapes_[unit][0].name + "\",\"" + shapes_[unit][1].name + "\"]";
         j += ",\"default_us\":[" + fmt(def_t_[unit][0]) + "," + fmt(def_t_[unit][1]) + "]";
         j += ",\"noise\":[" + fmt(noise_[unit][0]) + "," + fmt(noise_[unit][1]) + "]";
@@ -920,8 +1068,10 @@ int32_t Tuner::run(q8k4v_config* out_table, std::string* report) {
             cand_lists += "{\"stage\":\"" + c.stage + "\",\"cfg\":" + cfg_json(c.cfg) + ",\"verdict\":\"" + c.verdict +
                           "\",\"us\":[" + fmt(c.t[0]) + "," + fmt(c.t[1]) + "],\"dev\":[" + fmt(c.dev[0]) + "," +
                           fmt(c.dev[1]) + "],\"cost\":" + fmt(c.cost) + ",\"seq\":" + std::to_string(c.seq) +
-                          ",\"vt\":[" + (c.vt[0] < 0 ? std::string("null") : fmt(c.vt[0])) + "," +
-                          (c.vt[1] < 0 ? std::string("null") : fmt(c.vt[1])) + "]";
+                          ",\"vt\":[";
+            for (int k = 0; k < n_units_; ++k)
+                cand_lists += (k ? "," : "") + (c.vt[k] < 0 ? std::string("null") : fmt(c.vt[k]));
+            cand_lists += "]";
             cand_lists += ",\"ref_dev\":[" + fmt(c.ref_dev[0]) + "," + fmt(c.ref_dev[1]) + "]";
             if (!c.gate.empty()) cand_lists += ",\"gate\":\"" + c.gate + "\"";
             if (!c.why.empty()) cand_lists += ",\"why\":\"" + json_text(c.why) + "\"";
@@ -961,13 +1111,26 @@ extern "C" int32_t tune_select(const q8k4v_tune_request* req, q8k4v_config* out_
     if (req->n_draft < 1 || req->n_draft > Q8K4V_MAX_DRAFT) return fail(Q8K4V_EINVAL, "tune_select: n_draft must be in 1..16");
     if (req->ctx_small < 1 || req->ctx_large < req->ctx_small)
         return fail(Q8K4V_EINVAL, "tune_select: need 1 <= ctx_small <= ctx_large");
-    for (int k = 0; k < 4; ++k) {
+    if (req->n_sessions != 0 && (req->n_sessions < 2 || req->n_sessions > kMaxSessions ||
+                                 (int64_t)req->n_sessions * g > kMaxPrefixRows))
+        return fail(Q8K4V_EINVAL, "tune_select: n_sessions must be 0 or 2.." + std::to_string(kMaxSessions) +
+                                      " with n_sessions * group <= " + std::to_string(kMaxPrefixRows));
+    for (int k = 0; k < 6; ++k) {
         const q8k4v_tune_ref& r = req->ref[k];
         if (!r.cache) continue;
-        const int n = k >= 2 ? req->n_draft : 1;
-        if (!r.q || !r.page_table || !r.out || r.len < n || r.max_pages < 1 ||
-            (int64_t)r.max_pages * Q8K4V_PAGE_SIZE < r.len)
-            return fail(Q8K4V_EINVAL, "tune_select: inconsistent reference inputs for term " + std::to_string(k));
+        const std::string term = "tune_select: inconsistent reference inputs for term " + std::to_string(k);
+        if (!r.q || !r.page_table || !r.out || r.max_pages < 1 || (int64_t)r.max_pages * Q8K4V_PAGE_SIZE < r.len)
+            return fail(Q8K4V_EINVAL, term);
+        if (k < 4) {
+            if (r.len < (k >= 2 ? req->n_draft : 1)) return fail(Q8K4V_EINVAL, term);
+            continue;
+        }
+        if (req->n_sessions == 0)
+            return fail(Q8K4V_EINVAL, "tune_select: a multi-session reference (term " + std::to_string(k) +
+                                          ") needs n_sessions >= 2");
+        if (!r.seq_lens || r.n_seqs < 1 || (int64_t)r.n_seqs * g > kMaxPrefixRows || r.n_prefix_pages < 1 ||
+            r.n_prefix_pages > r.max_pages || (int64_t)r.n_prefix_pages * Q8K4V_PAGE_SIZE > r.len)
+            return fail(Q8K4V_EINVAL, term);
     }
     const int64_t budget = std::max<int64_t>(0, std::min<int64_t>(req->budget_ms, kMaxBudgetMs));
     Tuner t(*req, t0 + std::chrono::milliseconds(budget));

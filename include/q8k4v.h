@@ -227,9 +227,10 @@ int32_t attn_decode_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
  *                   output is undefined (with page ids in range no access
  *                   leaves the pools).
  *                   0 runs attn_decode_q8k4v.
- *   cfg             applies to the suffix pass (NULL: the decode defaults
- *                   with wgs_per_cu 4); the prefix pass uses the row-block
- *                   kernel's defaults
+ *   cfg             applies to the suffix pass (NULL: the configuration
+ *                   tune_select installed for this device and head shape, else
+ *                   the decode defaults with wgs_per_cu 4); the prefix pass
+ *                   uses the row-block kernel's defaults
  *   workspace       at least q8k4v_prefix_workspace_bytes(...) bytes
  * Other arguments as attn_decode_q8k4v.  Errors as attn_decode_q8k4v, plus
  * EINVAL for n_prefix_pages outside 0 .. min(max_pages, max_seq_len / 16)
@@ -394,8 +395,9 @@ int32_t q8k4v_stream_probe(const void *buf, size_t bytes, int32_t waves_per_wg, 
  * tune_select -- on-device search of the attention launch configuration
  * (blog.123qwe.co.kr/?p=3927, section 3: first-load tuner).
  *
- * For each unit (decode, verify) it measures candidate configurations on
- * four shapes -- decode and verify at ctx_small and ctx_large -- and keeps,
+ * For each unit (decode, verify, and with n_sessions the multi-session
+ * decode) it measures candidate configurations on its two shapes -- at
+ * ctx_small and ctx_large -- and keeps,
  * per unit, the admitted candidate with the least service cost
  *     cost(c) = sum over the unit's shapes p of median_time(c, p) / median_time(default, p)
  * (term weights 1, one launch per layer-step).  Every step -- allocation,
@@ -410,10 +412,10 @@ int32_t q8k4v_stream_probe(const void *buf, size_t bytes, int32_t waves_per_wg, 
  * candidate's deviation from the default configuration's output must not
  * exceed alpha times the storage-resolution noise, i.e. the change of the
  * default output when every stored code is moved by one step; and, on each
- * of the four terms for which the caller supplies a reference output (the
- * oracle gate: "keep only configurations whose output matches the oracle"),
- * the sigma-normalised deviation from it must not exceed ref_tol.  Search
- * order (section 3): after both defaults, each next candidate comes from the
+ * term for which the caller supplies a reference output (the oracle gate:
+ * a configuration is kept only if it reproduces the oracle), the
+ * sigma-normalised deviation from it must not exceed ref_tol.  Search
+ * order (section 3): after the units' defaults, each next candidate comes from the
  * unit with the earliest virtual completion time (effort + price) / (share x
  * opportunity) -- wall time spent on the unit, wall time of its last
  * measurement, its part of the default service time, the fraction of its
@@ -421,30 +423,37 @@ int32_t q8k4v_stream_probe(const void *buf, size_t bytes, int32_t waves_per_wg, 
  * before launch-shape refinement, and only configurations the library
  * accepts.  The JSON report lists every candidate with its verdict, the gate
  * that rejected it ("alpha" or "oracle") and why, its deviations (null where
- * not measured: unknown, never 0), its measurement order ("seq") and both
- * units' virtual times when it was picked ("vt"); each unit's summary counts
+ * not measured: unknown, never 0), its measurement order ("seq") and every
+ * unit's virtual time when it was picked ("vt"); each unit's summary counts
  * the rejections per gate and lists the distinct reasons of invalid
  * candidates.
  *
  *   req         host, see q8k4v_tune_request
- *   out_table   host [2]: [0] decode, [1] verify; `qualified` = 1 if a
- *               measured candidate was admitted, else the defaults with 0
+ *   out_table   host [2] ([3] when req->n_sessions >= 2): [0] decode,
+ *               [1] verify, [2] the multi-session suffix pass; `qualified` = 1
+ *               if a measured candidate was admitted, else the defaults with 0
  *   report_json host buffer for a JSON report (may be NULL), NUL-terminated
  * Returns Q8K4V_OK even when nothing could be searched (defaults,
  * unqualified); ENOMEM if memory admission refuses even the defaults;
  * EINVAL on bad shapes; EHIP.
  */
-/* One reference term of the tuner's oracle gate: a sequence in the caller's
- * cache with its expected attention output (e.g. from a CPU oracle). */
+/* One reference term of the tuner's oracle gate: sequences in the caller's
+ * cache with their expected attention output (e.g. from a CPU oracle). */
 typedef struct q8k4v_tune_ref {
     const q8k4v_cache *cache;          /* device pools; NULL: no reference for this term  */
     const void *q;                     /* device bf16 [n][num_q_heads][D]; n = 1 for the
-                                          decode terms, n_draft for the verify terms      */
-    const int32_t *page_table;         /* device int32 [max_pages]: the sequence's pages  */
-    int32_t len, max_pages;            /* tokens attended (the drafts included for verify) */
+                                          decode terms, n_draft for the verify terms,
+                                          n_seqs for the multi-session terms             */
+    const int32_t *page_table;         /* device int32 [max_pages]: the sequence's pages;
+                                          multi-session terms [n_seqs][max_pages]        */
+    int32_t len, max_pages;            /* tokens attended (the drafts included for
+                                          verify); multi-session: the longest session    */
     const float *out;                  /* host float32 [n][num_q_heads][D]                */
     const float *sigma;                /* host float32 [num_q_heads][D] or NULL (1): the
                                           deviation is |out - ref| / sigma per element    */
+    const int32_t *seq_lens;           /* multi-session terms: device int32 [n_seqs]     */
+    int32_t n_seqs;                    /* multi-session terms: sessions                  */
+    int32_t n_prefix_pages;            /* multi-session terms: leading shared pages      */
 } q8k4v_tune_ref;
 
 typedef struct q8k4v_tune_request {
@@ -458,19 +467,27 @@ typedef struct q8k4v_tune_request {
                                           (n_draft, num_q_heads, num_kv_heads, head_dim);
                                           the decode unit is stored under n_draft 1 */
     int32_t max_candidates;            /* 0: no limit */
+    int32_t n_sessions;                /* 0: two units; 2 .. 64: also the multi-session
+                                          unit -- attn_decode_prefix_q8k4v of n_sessions
+                                          sessions over a shared prefix (its suffix-pass
+                                          configuration is what is tuned); at ctx
+                                          (ctx_small, ctx_large) the sessions share a
+                                          ctx / 2 token prefix and session i owns about
+                                          (i + 1) / n_sessions x ctx / 2 more tokens    */
     /* Oracle gate (optional per term; the tuner never computes references
        itself): ref[k] for term k = decode@ctx_small, decode@ctx_large,
-       verify@ctx_small, verify@ctx_large.  A term with ref[k].cache != NULL
-       runs every candidate on the caller's inputs and admits it only if
+       verify@ctx_small, verify@ctx_large, multi-session small, multi-session
+       large.  A term with ref[k].cache != NULL runs every candidate on the
+       caller's inputs and admits it only if
        max |out - ref[k].out| / ref[k].sigma <= ref_tol.  The default must pass
        too, else the unit keeps unqualified defaults. */
-    q8k4v_tune_ref ref[4];
+    q8k4v_tune_ref ref[6];
     float ref_tol;                     /* tolerance on the normalised deviation            */
     float softmax_scale;               /* 0: 1/sqrt(D)                                      */
     /* optional text file of stored choices (may be NULL): a call whose device
        identity (architecture, device name and CU count, HIP runtime and driver
        versions, library build) and request shape (n_draft, head counts,
-       head_dim, ctx_small, ctx_large) match stored records uses them without
+       head_dim, ctx_small, ctx_large, n_sessions) match stored records uses them without
        measuring (report status "stored"); otherwise it searches and, when the
        search ran, replaces the records of that identity and shape (other
        records are kept) */

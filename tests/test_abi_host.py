@@ -208,6 +208,38 @@ def test_tuner_rejects_bad_requests(lib):
     assert lib.tune_select(C.byref(r), table, None, 0) == -1
 
 
+def test_tuner_rejects_bad_session_requests(lib):
+    """The multi-session unit: a session count of 2..64, and its reference
+    terms only with it and with their lengths, sessions and prefix."""
+    def req(**kw):
+        r = q8.TuneRequest()
+        for k, v in {**dict(num_q_heads=32, num_kv_heads=8, head_dim=128, n_draft=8, ctx_small=4096,
+                            ctx_large=65536, budget_ms=1000), **kw}.items():
+            setattr(r, k, v)
+        return r
+    table = (q8.Config * 3)()
+    for ns in (1, -2, 65):
+        assert lib.tune_select(C.byref(req(n_sessions=ns)), table, None, 0) == -1
+        assert b"n_sessions" in lib.q8k4v_last_error()
+    d = q8.CacheDesc(64, 8, 128, 16, 1, 1, 1, 1)
+    def with_ref(ns, **kw):
+        r = req(n_sessions=ns)
+        t = r.ref[4]
+        t.cache = C.pointer(d)
+        t.q, t.page_table, t.out, t.seq_lens = 1, 1, 1, 1
+        t.len, t.max_pages, t.n_seqs, t.n_prefix_pages = 600, 64, 4, 16
+        for k, v in kw.items():
+            setattr(t, k, v)
+        return lib.tune_select(C.byref(r), table, None, 0)
+    assert with_ref(0) == -1 and b"needs n_sessions" in lib.q8k4v_last_error()
+    assert with_ref(4, seq_lens=None) == -1 and b"term 4" in lib.q8k4v_last_error()
+    assert with_ref(4, n_seqs=0) == -1
+    assert with_ref(4, n_prefix_pages=0) == -1
+    assert with_ref(4, n_prefix_pages=65) == -1     # more shared pages than the table holds
+    assert with_ref(4, len=200) == -1               # shorter than the shared prefix
+    assert with_ref(4, n_seqs=1100) == -1           # 1100 sessions x 4 rows: prefix block too large
+
+
 def test_binding_rejects_host_tensors():
     """The binding hands raw device pointers to the library: host tensors are
     refused before any call (no CPU path)."""

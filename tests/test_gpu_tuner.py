@@ -3,7 +3,8 @@ first-load tuner of blog.123qwe.co.kr/?p=3927, section 3, admission rule of
 section 4): the wall-clock budget holds, timing rotates past the last-level
 cache, every admitted configuration reproduces the oracle, a tiny budget or
 failing references leave the defaults unqualified, and installed winners are
-used by calls without a config."""
+used by calls without a config; with n_sessions the multi-session unit (the
+shared-prefix entry point's suffix pass) is searched and gated the same way."""
 
 import json
 import time
@@ -20,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def _tune(**kw):
     import decode_attention_quantized_kv_amd as q8
     t0 = time.perf_counter()
-    dcfg, vcfg, rep = q8.tune_select(**kw)
+    dcfg, vcfg, _, rep = q8.tune_select(**kw)
     wall = time.perf_counter() - t0
     print("[tuner]", json.dumps({k: v for k, v in rep.items() if k != "candidates"}), flush=True)
     return dcfg, vcfg, rep, wall
@@ -188,7 +189,7 @@ def test_tuner_records_reuse_and_identity_change(tmp_path):
     ident = rep1["identity_hash"]
     assert "arch=gfx950" in rep1["identity"] and "library=q8k4v" in rep1["identity"]
     lines = open(path).read().splitlines()
-    assert len(lines) == 2 and all(l.split()[:3] == ["q8k4v-tune-record", "1", ident] for l in lines)
+    assert len(lines) == 2 and all(l.split()[:3] == ["q8k4v-tune-record", "2", ident] for l in lines)
     # the same identity and shape: the stored choice, nothing measured
     d2, v2, rep2, wall = _tune(**kw)
     assert rep2["status"] == "stored" and rep2["record"] == "loaded"
@@ -206,3 +207,63 @@ def test_tuner_records_reuse_and_identity_change(tmp_path):
     assert rep3["status"] == "searched" and rep3["record"] == "stored"
     hashes = [l.split()[2] for l in open(path).read().splitlines()]
     assert hashes.count("0123456789abcdef") == 4 and hashes.count(ident) == 2 and len(hashes) == 6
+
+
+def _session_references(hq, hkv, D, ns, seed):
+    """Oracle references for the multi-session terms: ns ragged sessions over
+    a 256-token (small) and a 2048-token (large) shared prefix."""
+    from tests.gpu_util import to_dev, upload_cache
+    from tests.util import sigma_q_heads
+    rng = np.random.default_rng(seed)
+    refs = {}
+    for size, pre, suf in (("small", 256, 300), ("large", 2048, 1500)):
+        w = workloads.build("tref_ms_" + size, seed=seed + pre, num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
+                            dtype="bf16", seq_lens=pre + rng.integers(0, suf, size=ns), shared_prefix=pre,
+                            outliers=True)
+        refs["multi_session_" + size] = {
+            "cache": upload_cache(w), "q": to_dev(w.q, "bf16"), "page_table": to_dev(w.page_table),
+            "length": int(max(w.seq_lens)), "seq_lens": to_dev(w.seq_lens), "n_prefix_pages": pre // 16,
+            "out": oracle_out(w).astype(np.float32), "sigma": sigma_q_heads(w)}
+    return refs
+
+
+def test_tuner_multi_session_unit():
+    """n_sessions adds a third unit: it is searched in the same virtual-time
+    order, never with the in-launch merge, every admitted candidate matches
+    the oracle on both multi-session terms, and the installed winner serves
+    the shared-prefix entry point without a config, at parity."""
+    import decode_attention_quantized_kv_amd as q8
+    from tests.gpu_util import run_prefix, upload_cache
+    hq, hkv, D, NS = 16, 4, 128, 4
+    refs = _session_references(hq, hkv, D, NS, seed=80)
+    t0 = time.perf_counter()
+    dcfg, vcfg, mcfg, rep = q8.tune_select(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, n_draft=4,
+                                           ctx_small=1024, ctx_large=8192, budget_ms=9000, seed=8, install=True,
+                                           refs=refs, ref_tol=ATOL_SIGMA, n_sessions=NS)
+    wall = time.perf_counter() - t0
+    print("[tuner]", json.dumps({k: v for k, v in rep.items() if k != "candidates"}), flush=True)
+    assert rep["status"] == "searched" and wall * 1e3 <= 9000 + 3000
+    assert len(rep["units"]) == 3 and len(rep["candidates"]) == 3
+    ms, cands = rep["units"][2], rep["candidates"][2]
+    assert ms["unit"] == "multi_session" and ms["sessions"] == NS and ms["rows_per_kv_head"] == hq // hkv
+    assert ms["oracle_gate"] == [True, True] and rep["units"][0]["oracle_gate"] == [False, False]
+    assert ms["invalid"] == 0, ms["invalid_why"]
+    assert cands[0]["stage"] == "default" and cands[0]["verdict"] == "admitted" and len(cands) >= 2
+    assert ms["qualified"] and mcfg.qualified == 1
+    assert {k: getattr(mcfg, k) for k in ms["chosen"]} == ms["chosen"]
+    for c in cands:
+        assert c["cfg"]["fused_combine"] == 0
+        if c["verdict"] == "admitted":
+            assert max(c["ref_dev"]) <= ATOL_SIGMA
+            assert max(c["dev"]) <= rep["alpha"] * max(ms["noise"])
+    # the order over three units: each pick had the least virtual time
+    picked = [(u, c) for u, cs in enumerate(rep["candidates"]) for c in cs if c["stage"] != "default" and c["seq"] >= 0]
+    assert 2 in {u for u, _ in picked}
+    for u, c in picked:
+        assert len(c["vt"]) == 3 and c["vt"][u] is not None
+        assert all(v is None or c["vt"][u] <= v for v in c["vt"])
+    # the installed winner serves calls without a config
+    w = workloads.build("ms_after_tune", seed=81, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, dtype="bf16",
+                        seq_lens=[700, 513, 1200, 512, 999], shared_prefix=512, outliers=True)
+    err = normalized_err(w, run_prefix(w, upload_cache(w), 32), oracle_out(w))
+    assert err <= ATOL_SIGMA, err

@@ -6,7 +6,8 @@ oracle and the HIP path consume exactly the arrays built here.
 
 Recipe (numpy ``default_rng(seed)``; draw order fixed: queries, keys,
 values, key outlier channels, value outlier channels, page permutation; the
-multi-session suffix lengths come from ``default_rng(seed + 1000)``):
+multi-session suffix lengths come from ``default_rng(seed + 1000)``, those of
+the tuner's session references from ``default_rng(seed + 3000)``):
 
 * queries, keys and values are standard normal, drawn in float32;
 * "outlier channels": ``round(0.01 * Hkv * D)`` (kv head, dim) channels are
@@ -245,6 +246,19 @@ def tune_reference(context: int, n_draft: int = 8, seed: int = 11) -> Workload:
     them with every draft."""
     return build(f"tune_ref_{context}_w{n_draft}", seed=seed, num_q_heads=32, num_kv_heads=8, head_dim=128,
                  dtype="bf16", seq_lens=[context + n_draft], n_draft=n_draft, outliers=True)
+
+
+def tune_sessions_reference(context: int, sessions: int = 16, seed: int = 13) -> Workload:
+    """Caller inputs of the tuner's multi-session oracle terms at one context:
+    ``sessions`` sessions (32 query / 4 kv heads, D 128, bf16, 1 % outlier
+    channels x8) over one ``context / 2`` token shared prefix, each with a
+    private suffix of uniform-random 1..context/2 tokens (the length mix of
+    the 16-session workload, at ``context`` 65536)."""
+    half = context // 2
+    rng = np.random.default_rng(seed + 3000)
+    suffix = rng.integers(1, half + 1, size=sessions)
+    return build(f"tune_ref_sessions_{sessions}x{half}", seed=seed, num_q_heads=32, num_kv_heads=4, head_dim=128,
+                 dtype="bf16", seq_lens=half + suffix, outliers=True, shared_prefix=half)
 
 
 NAMED = {
