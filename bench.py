@@ -41,6 +41,7 @@ LLC_BYTES = 256 << 20
 WORKLOADS = ["tiny_decode_256", "gqa_decode_4096", "gqa_decode_65536", "verify_65536_w8", "multi_session_16x32768"]
 TUNE_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q8kv_d128_w8.npz")
 TUNE_SESSION_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q4kv_d128_s16.npz")
+MAX_LAYERS = 512
 
 
 def cache_bytes_per_token_head(D: int, affine: bool = False) -> int:
@@ -201,7 +202,11 @@ def run_workload(args, torch, q8, w, cfg, tuned, full_line: bool) -> dict:
     per_th = cache_bytes_per_token_head(D, args.codec == "affine")
     unique = w.unique_tokens()
     layer_bytes = w.num_pages * H * 16 * per_th
-    layers = args.layers or max(2, -(-4 * LLC_BYTES // layer_bytes) + 1)
+    # enough distinct layer caches that the rotation streams 4x the LLC, at
+    # most MAX_LAYERS: a cache of a few pages (the 256-token workload) stays
+    # LLC-resident whatever the rotation, and tens of thousands of caches
+    # would only slow the setup
+    layers = args.layers or min(MAX_LAYERS, max(2, -(-4 * LLC_BYTES // layer_bytes) + 1))
     K = args.steps
 
     bf = w.dtype == "bf16"
@@ -353,10 +358,13 @@ def run_workload(args, torch, q8, w, cfg, tuned, full_line: bool) -> dict:
 def attention_launch_name(nd, n_pref, w, cfg, q8) -> str:
     if n_pref:
         return "attn_decode_prefix_q8k4v launch (prefix and suffix passes + cascade combine kernel)"
+    entry = "attn_verify_q8k4v" if nd else "attn_decode_q8k4v"
+    msl = int(w.seq_lens.max())
+    if q8.workspace_bytes(w.n_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, msl, max(1, nd), cfg) == 0:
+        return entry + " launch (one split per sequence and kv head: the attention kernel alone)"
     fused = bool(cfg and cfg.fused_combine)
-    return ("attn_verify_q8k4v" if nd else "attn_decode_q8k4v") + (
-        " launch (split-K attention kernel with the in-launch split merge)" if fused else
-        " launch (split-K attention kernel + LSE combine kernel)")
+    return entry + (" launch (split-K attention kernel with the in-launch split merge)" if fused else
+                    " launch (split-K attention kernel + LSE combine kernel)")
 
 
 def run_probes(torch, q8, caches, seq_lens, msl, page_table, K, layers, cache_read, w, n_pref):

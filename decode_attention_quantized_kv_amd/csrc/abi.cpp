@@ -186,6 +186,11 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     int32_t sp;
     if (cfg.split_pages > 0) {
         sp = round_up(cfg.split_pages, unit);
+    } else if (max_np <= unit * cfg.stages) {
+        // one workgroup has every page of the sequence in flight at once (each
+        // wave's ring holds its share): splitting cannot shorten that one
+        // round trip and would add the merge
+        sp = round_up(max_np, unit);
     } else {
         const int64_t target = (int64_t)cfg.wgs_per_cu * device_cu_count();
         const int64_t per = (int64_t)a.n_seqs * H * plan->row_chunks;
