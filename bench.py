@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 WORKLOADS = ["tiny_decode_256", "gqa_decode_4096", "gqa_decode_65536", "verify_65536_w8", "multi_session_16x32768"]
+LONG_WORKLOADS = ["gqa_decode_131072", "gqa_decode_200000", "verify_131072_w8", "verify_200000_w8"]
 TUNE_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q8kv_d128_w8.npz")
 TUNE_SESSION_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q4kv_d128_s16.npz")
 MAX_LAYERS = 512
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa_decode_65536", choices=WORKLOADS + ["all"],
+    ap.add_argument("--workload", default="gqa_decode_65536", choices=WORKLOADS + LONG_WORKLOADS + ["all"],
                     help="all: one JSON line per workload (attention launches, no CPU baseline)")
     ap.add_argument("--layers", type=int, default=0, help="rotating layer caches (0: enough for 4x LLC)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -267,4 +267,9 @@ NAMED = {
     "gqa_decode_65536": gqa_decode_64k,
     "verify_65536_w8": verify_64k,
     "multi_session_16x32768": multi_session,
+    # longer contexts of the same shapes (timed on request, not in every run)
+    "gqa_decode_131072": lambda: gqa_decode(131072, 5),
+    "gqa_decode_200000": lambda: gqa_decode(200000, 6),
+    "verify_131072_w8": lambda: verify_64k(7, 131072, 8),
+    "verify_200000_w8": lambda: verify_64k(8, 200000, 8),
 }
