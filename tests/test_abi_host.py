@@ -111,6 +111,23 @@ def test_workspace_size_follows_the_plan(lib):
     assert q8.workspace_bytes(1, 4, 4, 128, 4096, 0, q8.make_config(tile_pages=4)) == 0
 
 
+def test_sequences_that_fit_in_flight_are_not_split(lib):
+    """The automatic plan does not split a sequence whose pages all fit in
+    one workgroup's rings at once (waves x 2-page tiles x stages: 16 pages,
+    256 tokens, at the decode defaults of 4 waves and 2 stages): no split
+    records, so no workspace; one page more and it splits."""
+    for hq, hkv, d in ((2, 1, 64), (32, 8, 128)):
+        assert q8.workspace_bytes(1, hq, hkv, d, 256) == 0
+        assert q8.workspace_bytes(4, hq, hkv, d, 256) == 0
+        assert q8.workspace_bytes(1, hq, hkv, d, 257) > 0
+    # 8 waves or 3 stages hold more pages in flight
+    assert q8.workspace_bytes(1, 32, 8, 128, 512, 0, q8.make_config(waves_per_wg=8)) == 0
+    assert q8.workspace_bytes(1, 32, 8, 128, 384, 0, q8.make_config(stages=3)) == 0
+    assert q8.workspace_bytes(1, 32, 8, 128, 400, 0, q8.make_config(stages=3)) > 0
+    # an explicit split length still splits
+    assert q8.workspace_bytes(1, 32, 8, 128, 256, 0, q8.make_config(split_pages=8)) > 0
+
+
 def test_workspace_header_is_shared_by_every_plan(lib):
     """Every plan that writes split records puts them behind one fixed
     header, and the in-launch merge keeps its counters inside that header:
