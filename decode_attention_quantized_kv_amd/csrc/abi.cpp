@@ -229,9 +229,6 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     }
     if (plan->split_pages > 64 * cfg.waves_per_wg)
         return fail(Q8K4V_EUNSUPPORTED, "attention: sequence too long (more than 1024 splits of 64 pages per wave)");
-    // a multiple of 8 splits lets the kernels deal each sequence's splits
-    // round robin over the 8 XCDs (the extra splits hold no pages)
-    if (plan->n_splits > 1) plan->n_splits = round_up(plan->n_splits, 8);
     // the in-launch merge keeps one arrival counter per (sequence, kv head,
     // row chunk) in the workspace header; a launch with more items than the
     // header holds merges with the separate combine kernel instead
@@ -360,7 +357,6 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     spp = std::min(std::max(spp, unit), 64 * pp.waves);
     pp.split_pages = spp;
     pp.n_splits = (n_pref + spp - 1) / spp;
-    if (pp.n_splits > 1) pp.n_splits = round_up(pp.n_splits, 8);
     pp.fused_combine = 0;
     pp.counter_bytes = 0;
     pp.partial_bytes = round256((size_t)H * pp.n_splits * pp.rows * rec);

@@ -59,32 +59,26 @@ struct WorkItem {
 };
 
 // Work items are (sequence, split, kv head, row chunk); the dispatcher hands
-// workgroup i to XCD i % 8.  The kv heads and row chunks of one (sequence,
-// split) -- which share the lines of the key-scale pool -- stay on one XCD's
-// L2.  With a split count that is a multiple of 8, split s of sequence b goes
-// to XCD (s + b) mod 8: every sequence's splits are dealt round robin over
-// the XCDs, starting at a different XCD per sequence, so a ragged batch
-// loads the XCDs evenly.  Otherwise XCD x takes the x-th eighth of the items
-// in order.
+// workgroup i to XCD i % 8.  The (sequence, split) pairs are taken split by
+// split -- every sequence's split 0, then every split 1, ... -- with the
+// sequences of split round s rotated by s, and dealt round robin over the 8
+// XCDs; the kv heads and row chunks of a pair (which share the lines of the
+// key-scale pool) stay together on its XCD.  So pair (s, b) sits at slot
+// q = s n + (b + s) mod n: a sequence's consecutive splits visit different
+// XCDs, every XCD gets an even share of the pairs with no slot left empty
+// but in the last round, and the workgroups that hold pages come first in
+// dispatch order -- in a batch of ragged lengths the empty splits of the
+// short sequences are the late ones -- so the workgroups with pages spread
+// over the CUs instead of pairing up on some of them.
 Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w, int bid) {
     const int C = p.H * p.row_chunks;          // items per (sequence, split)
+    const int n = p.n_seqs;
     const int x = bid & 7, j = bid >> 3;
-    int inner;
-    if ((p.n_splits & 7) == 0) {
-        const int S8 = p.n_splits >> 3;        // splits per sequence and XCD
-        inner = j % C;
-        const int t = j / C;
-        w.b = t / S8;
-        if (w.b >= p.n_seqs) return false;
-        w.split = ((x - w.b) & 7) + 8 * (t % S8);
-    } else {
-        const int total = p.n_seqs * p.n_splits * C;
-        const int item = x * ((total + 7) >> 3) + j;
-        if (item >= total) return false;
-        inner = item % C;
-        w.split = (item / C) % p.n_splits;
-        w.b = item / (C * p.n_splits);
-    }
+    const int inner = j % C;
+    const int q = 8 * (j / C) + x;             // pair slot, split-major
+    if (q >= n * p.n_splits) return false;
+    w.split = q / n;
+    w.b = (q % n - w.split % n + n) % n;
     w.rchunk = inner % p.row_chunks;
     w.kh = inner / p.row_chunks;
     if (p.page_cap > 0) {
@@ -99,6 +93,12 @@ Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w, int bid) {
     return true;
 }
 Q8K4V_DEV bool work_item(const AttnParams& p, WorkItem& w) { return work_item(p, w, (int)blockIdx.x); }
+
+// Workgroups of a launch under that mapping: 8 XCDs x rounds of pair slots x items per pair.
+inline int work_blocks(const AttnParams& p) {
+    const int slots = p.n_seqs * p.n_splits;
+    return 8 * ((slots + 7) / 8) * p.H * p.row_chunks;
+}
 
 Q8K4V_DEV size_t out_index(const AttnParams& p, int b, int kh, int r, int D) {
     const int j = r / p.G, g = r % p.G;

@@ -1124,8 +1124,7 @@ __global__ __launch_bounds__(256) void attn_cascade_kernel(const AttnParams pre,
 
 template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 hipError_t launch_rows_t(const AttnParams& kp, hipStream_t stream) {
-    const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
-    const int blocks = 8 * ((total + 7) / 8);
+    const int blocks = work_blocks(kp);
     hipLaunchKernelGGL((attn_rows_kernel<D, RB, WAVES, STAGES, QBF16, AFF>), dim3(blocks), dim3(64 * WAVES), 0, stream,
                        kp);
     return hipGetLastError();
@@ -1133,8 +1132,7 @@ hipError_t launch_rows_t(const AttnParams& kp, hipStream_t stream) {
 
 template <int D, int R, int WAVES, int STAGES, bool QBF16, bool AFF>
 hipError_t launch_t(const AttnParams& kp, hipStream_t stream) {
-    const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
-    const int blocks = 8 * ((total + 7) / 8);
+    const int blocks = work_blocks(kp);
     hipLaunchKernelGGL((attn_dec2_kernel<D, R, WAVES, STAGES, QBF16, AFF>), dim3(blocks), dim3(64 * WAVES), 0, stream,
                        kp);
     return hipGetLastError();
@@ -1189,10 +1187,8 @@ LaunchFn pick_rows(int rows_per_wg, int waves, int stages) {
 
 template <int D, int R, bool QBF16, bool AFF>
 hipError_t launch_cascade_t(const AttnParams& pre, const AttnParams& suf, hipStream_t stream) {
-    const int pre_total = pre.n_seqs * pre.H * pre.n_splits * pre.row_chunks;
-    const int pre_blocks = 8 * ((pre_total + 7) / 8);
-    const int suf_total = suf.n_seqs * suf.H * suf.n_splits * suf.row_chunks;
-    const int suf_blocks = 8 * ((suf_total + 7) / 8);
+    const int pre_blocks = work_blocks(pre);   // a multiple of 8: every block keeps its XCD
+    const int suf_blocks = work_blocks(suf);
     hipLaunchKernelGGL((attn_cascade_kernel<D, R, QBF16, AFF>), dim3(pre_blocks + suf_blocks), dim3(256), 0, stream,
                        pre, suf, pre_blocks);
     return hipGetLastError();
@@ -1209,8 +1205,7 @@ hipError_t pick_cascade(int rows, const AttnParams& pre, const AttnParams& suf, 
 
 template <int D, int R, bool QBF16, bool AFF>
 hipError_t launch_append_t(const AttnParams& kp, hipStream_t stream) {
-    const int total = kp.n_seqs * kp.H * kp.n_splits * kp.row_chunks;
-    const int blocks = 8 * ((total + 7) / 8);
+    const int blocks = work_blocks(kp);
     hipLaunchKernelGGL((attn_dec2_append_kernel<D, R, QBF16, AFF>), dim3(blocks), dim3(256), 0, stream, kp);
     return hipGetLastError();
 }

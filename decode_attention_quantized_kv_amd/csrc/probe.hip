@@ -120,8 +120,7 @@ __global__ __launch_bounds__(64 * WAVES) void stream_probe_kernel(const uint8_t*
 
 template <int D, int WAVES, int STAGES, int HPW>
 hipError_t launch_paged_probe_t(const AttnParams& kp, hipStream_t stream) {
-    const int total = kp.n_seqs * kp.H * kp.n_splits;
-    hipLaunchKernelGGL((paged_probe_kernel<D, WAVES, STAGES, HPW>), dim3(8 * ((total + 7) / 8)), dim3(64 * WAVES),
+    hipLaunchKernelGGL((paged_probe_kernel<D, WAVES, STAGES, HPW>), dim3(work_blocks(kp)), dim3(64 * WAVES),
                        0, stream, kp);
     return hipGetLastError();
 }
@@ -179,14 +178,13 @@ extern "C" int32_t q8k4v_hbm_probe(const q8k4v_cache* cache, int32_t n_seqs, con
     int32_t rc = make_plan(a, &cfg, &plan);
     if (rc != Q8K4V_OK) return rc;
     // heads_per_wg > 1: the same number of workgroups, each over hpw heads
-    // and 1/hpw of the pages (a multiple of 8 splits, at least a tile per wave)
+    // and 1/hpw of the pages (at least a tile per wave)
     int32_t split_pages = plan.split_pages, n_splits = plan.n_splits;
     if (hpw > 1) {
         const int32_t max_np = std::max(1, (max_seq_len + 15) / 16);
         const int32_t unit = 2 * (waves_per_wg / hpw);
         split_pages = std::max(unit, (plan.split_pages / hpw + unit - 1) / unit * unit);
         n_splits = (max_np + split_pages - 1) / split_pages;
-        if (n_splits > 1) n_splits = (n_splits + 7) / 8 * 8;
         if (split_pages > 64 * (waves_per_wg / hpw)) return fail(Q8K4V_EUNSUPPORTED, "q8k4v_hbm_probe: too long");
     }
     AttnParams kp{};

@@ -273,7 +273,7 @@ def test_long_context_splits_are_even(lib):
     """Beyond the 64-pages-per-wave cap, a one-chunk decode takes a whole
     number of workgroups per CU and a multiple of 8 splits (the workspace
     holds one (m, l, o[D]) record per split, kv head and row); prefill blocks
-    keep the capped split."""
+    keep the capped split, and no plan pads its split count."""
     import decode_attention_quantized_kv_amd as q8
     rec = 4 * (128 + 4)
 
@@ -284,8 +284,8 @@ def test_long_context_splits_are_even(lib):
     assert splits(65536) == 32 and splits(131072) == 32       # under the cap: one workgroup per CU
     for ctx in (163840, 200000, 262144):
         s = splits(ctx)
-        assert s == 64, (ctx, s)                             # two per CU, 8 per XCD
-    assert splits(65536 + 512, 512) == 16                    # 9 capped splits, padded to 16
+        assert 62 <= s <= 64, (ctx, s)                       # about two per CU (whole tiles per split)
+    assert splits(65536 + 512, 512) == 9                     # 9 capped splits (no padding)
 
 
 def test_probes_reject_bad_arguments(lib):

@@ -248,6 +248,23 @@ def tune_reference(context: int, n_draft: int = 8, seed: int = 11) -> Workload:
                  dtype="bf16", seq_lens=[context + n_draft], n_draft=n_draft, outliers=True)
 
 
+def multi_session_part(part: str, seed: int = 4, sessions: int = 16, prefix: int = 32768,
+                       max_suffix: int = 32768) -> Workload:
+    """One of the two passes of the 16-session workload on its own: "prefix"
+    -- every session the shared prefix and one token of its own (the
+    cascade's suffix pass is a single page per session) -- or "suffixes" --
+    the sessions' private suffixes (same lengths as the full workload) as
+    plain sequences without the prefix."""
+    rng = np.random.default_rng(seed + 1000)
+    suffix = rng.integers(0, max_suffix + 1, size=sessions)
+    if part == "prefix":
+        return build(f"multi_session_{sessions}x{prefix}_prefix", seed=seed, num_q_heads=32, num_kv_heads=4,
+                     head_dim=128, dtype="bf16", seq_lens=np.full(sessions, prefix + 1), outliers=True,
+                     shared_prefix=prefix)
+    return build(f"multi_session_{sessions}_suffixes", seed=seed, num_q_heads=32, num_kv_heads=4, head_dim=128,
+                 dtype="bf16", seq_lens=suffix, outliers=True)
+
+
 def tune_sessions_reference(context: int, sessions: int = 16, seed: int = 13) -> Workload:
     """Caller inputs of the tuner's multi-session oracle terms at one context:
     ``sessions`` sessions (32 query / 4 kv heads, D 128, bf16, 1 % outlier
@@ -272,4 +289,7 @@ NAMED = {
     "gqa_decode_200000": lambda: gqa_decode(200000, 6),
     "verify_131072_w8": lambda: verify_64k(7, 131072, 8),
     "verify_200000_w8": lambda: verify_64k(8, 200000, 8),
+    # the 16-session workload's two passes on their own
+    "multi_session_16x32768_prefix": lambda: multi_session_part("prefix"),
+    "multi_session_16_suffixes": lambda: multi_session_part("suffixes"),
 }
