@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 WORKLOADS = ["tiny_decode_256", "gqa_decode_4096", "gqa_decode_65536", "verify_65536_w8", "multi_session_16x32768"]
 LONG_WORKLOADS = ["gqa_decode_131072", "gqa_decode_200000", "verify_131072_w8", "verify_200000_w8",
-                  "multi_session_16x32768_prefix", "multi_session_16_suffixes"]
+                  "multi_session_16x32768_prefix", "multi_session_16_suffixes", "batch_decode_16x4096"]
 TUNE_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q8kv_d128_w8.npz")
 TUNE_SESSION_REFS = os.path.join(ROOT, "tests", "golden", "tune_refs_32q4kv_d128_s16.npz")
 MAX_LAYERS = 512

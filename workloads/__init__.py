@@ -289,6 +289,9 @@ NAMED = {
     "gqa_decode_200000": lambda: gqa_decode(200000, 6),
     "verify_131072_w8": lambda: verify_64k(7, 131072, 8),
     "verify_200000_w8": lambda: verify_64k(8, 200000, 8),
+    # a uniform batch: 16 sequences of 4096 tokens (as many cache bytes as the 64K decode)
+    "batch_decode_16x4096": lambda: build("batch_decode_16x4096", seed=9, num_q_heads=32, num_kv_heads=8,
+                                          head_dim=128, dtype="bf16", seq_lens=[4096] * 16, outliers=True),
     # the 16-session workload's two passes on their own
     "multi_session_16x32768_prefix": lambda: multi_session_part("prefix"),
     "multi_session_16_suffixes": lambda: multi_session_part("suffixes"),
