@@ -51,6 +51,15 @@ struct AttnParams {
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Online softmax reference (log2 units): a row's reference moves only when a
+// score passes it and is then set this far above the new maximum.  Every
+// p = 2^(s - ref) stays <= 1 (so p times an fp16 value scale stays finite in
+// fp16), the largest p of a row is >= 2^-kRefHeadroom, and the accumulators
+// are rescaled only when a score passes the reference rather than on every
+// new maximum.  Partial results carry the reference as their m, which is all
+// the log-sum-exp merge needs.
+constexpr float kRefHeadroom = 2.0f;
+
 template <int D>
 constexpr int partial_stride() { return D + 4; }   // m, l, pad, pad, o[D]
 

@@ -544,10 +544,10 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[u][i]);
         tmax = xgroups_max(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        const float ref = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = exp2_fast(m_run - ref);
-        m_run = m_new;
+        const float r_old = m_run;
+        const bool up = tmax > r_old;
+        m_run = up ? tmax + kRefHeadroom : r_old;
+        const float ref = (m_run == kNegInf) ? 0.0f : m_run;
         float psum = 0.0f;
 #pragma unroll
         for (int u = 0; u < TP; ++u)
@@ -556,8 +556,11 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
                 s[u][i] = exp2_fast(s[u][i] - ref);
                 psum += s[u][i];
             }
-        l_run = l_run * alpha + psum;
-        if (__builtin_amdgcn_ballot_w64(alpha < 1.0f) != 0) {
+        if (__builtin_amdgcn_ballot_w64(up && r_old != kNegInf) != 0) {
+            // 0 on rows that had no finite score yet (their sums are 0), 1 on
+            // rows whose reference did not move
+            const float alpha = exp2_fast(r_old - ref);
+            l_run *= alpha;
             // output rows 4q4 + i hold query row (4q4 + i) mod R
             float ai[4];
             if (R <= 4) {
@@ -575,6 +578,7 @@ Q8K4V_DEV void dec2_body(const AttnParams& p, uint8_t* smem, int bid) {
                 acc[dt][0] *= ai[0]; acc[dt][1] *= ai[1]; acc[dt][2] *= ai[2]; acc[dt][3] *= ai[3];
             }
         }
+        l_run += psum;
         // ---- A operands: P' = p * value scale, rounded once to fp16; half
         // 2j + u of the lane = page u, token 4q4 + j
         u32x4 pa[NA];
@@ -953,10 +957,10 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[u][i]);
             tmax = xgroups_max(tmax);
-            const float m_new = fmaxf(m_run[rb], tmax);
-            const float ref = (m_new == kNegInf) ? 0.0f : m_new;
-            const float alpha = exp2_fast(m_run[rb] - ref);
-            m_run[rb] = m_new;
+            const float r_old = m_run[rb];
+            const bool up = tmax > r_old;
+            m_run[rb] = up ? tmax + kRefHeadroom : r_old;
+            const float ref = (m_run[rb] == kNegInf) ? 0.0f : m_run[rb];
             float psum = 0.0f;
 #pragma unroll
             for (int u = 0; u < TP; ++u)
@@ -965,8 +969,9 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                     s[u][i] = exp2_fast(s[u][i] - ref);
                     psum += s[u][i];
                 }
-            l_run[rb] = l_run[rb] * alpha + psum;
-            if (__builtin_amdgcn_ballot_w64(alpha < 1.0f) != 0) {
+            if (__builtin_amdgcn_ballot_w64(up && r_old != kNegInf) != 0) {
+                const float alpha = exp2_fast(r_old - ref);
+                l_run[rb] *= alpha;
                 float ai[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * q4 + i);   // lane 4q4+i holds that row
@@ -975,6 +980,7 @@ Q8K4V_DEV void rows_body(const AttnParams& p, uint8_t* smem, int bid) {
                     acc[rb][dt][0] *= ai[0]; acc[rb][dt][1] *= ai[1]; acc[rb][dt][2] *= ai[2]; acc[rb][dt][3] *= ai[3];
                 }
             }
+            l_run[rb] += psum;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 pp[rb][j] = as_u32(__builtin_convertvector(
