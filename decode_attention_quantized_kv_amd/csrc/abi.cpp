@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -180,7 +179,7 @@ int32_t make_plan(const AttnArgs& a, const q8k4v_config* cfg_in, Plan* plan) {
     plan->tile_pages = cfg.tile_pages;
     plan->waves = cfg.waves_per_wg;
     plan->stages = cfg.stages;
-    plan->rows_per_wg = kernel == kRows ? ((rows > 16 && !getenv("Q8K4V_EXP_RW16")) ? 32 : 16) : rows;
+    plan->rows_per_wg = kernel == kRows ? (rows > 16 ? 32 : 16) : rows;
     plan->row_chunks = (rows + plan->rows_per_wg - 1) / plan->rows_per_wg;
     const int32_t max_np = std::max(1, (a.max_seq_len + Q8K4V_PAGE_SIZE - 1) / Q8K4V_PAGE_SIZE);
     const int32_t unit = cfg.tile_pages * cfg.waves_per_wg;      // pages per workgroup step
@@ -346,7 +345,7 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
                       sp.stages == 2;
     pp.waves = (rows > 16 && !fuse) ? 8 : 4;
     pp.stages = 2;
-    pp.rows_per_wg = (rows > 16 && !(fuse && getenv("Q8K4V_EXP_PRE16"))) ? 32 : 16;
+    pp.rows_per_wg = rows > 16 ? 32 : 16;
     pp.row_chunks = (pp.rows + pp.rows_per_wg - 1) / pp.rows_per_wg;
     const int32_t unit = pp.tile_pages * pp.waves;
     const int64_t per = (int64_t)H * pp.row_chunks;

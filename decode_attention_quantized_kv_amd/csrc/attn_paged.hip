@@ -1110,11 +1110,8 @@ template <int D, int RB, int WAVES, int STAGES, bool QBF16, bool AFF>
 __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[WAVES * STAGES * ring_stage_bytes<D, AFF>()];
     // the shared query operands (RB x 3 KiB per 64 dimensions) where the LDS
-    // budget allows them; a one-block workgroup of fewer than 8 waves
-    // converts its 16 rows per wave instead and keeps its LDS small enough
-    // for three workgroups per CU
-    constexpr bool SQ = (RB > 1 || WAVES >= 8) &&
-                        WAVES * STAGES * ring_stage_bytes<D, AFF>() + RB * (D / 64) * 3072 + 8192 <= 163840;
+    // budget allows them
+    constexpr bool SQ = WAVES * STAGES * ring_stage_bytes<D, AFF>() + RB * (D / 64) * 3072 + 8192 <= 163840;
     rows_body<D, RB, WAVES, STAGES, QBF16, AFF, SQ>(p, s_stage, (int)blockIdx.x);
 }
 
@@ -1124,10 +1121,10 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
 // one tile ring per workgroup.  Both are four-wave, two-stage rings, so a
 // compute-bound prefix workgroup and memory-bound suffix workgroups share
 // each CU.  pre_blocks is a multiple of 8, which keeps every block's XCD.
-template <int D, int R, int PRB, bool QBF16, bool AFF>
+template <int D, int R, bool QBF16, bool AFF>
 __global__ __launch_bounds__(256) void attn_cascade_kernel(const AttnParams pre, const AttnParams suf, int pre_blocks) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, AFF>()];
-    if ((int)blockIdx.x < pre_blocks) rows_body<D, PRB, 4, 2, QBF16, AFF>(pre, s_stage, (int)blockIdx.x);
+    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16, AFF>(pre, s_stage, (int)blockIdx.x);
     else dec2_body<D, R, 4, 2, QBF16, AFF>(suf, s_stage, (int)blockIdx.x - pre_blocks);
 }
 
@@ -1198,13 +1195,8 @@ template <int D, int R, bool QBF16, bool AFF>
 hipError_t launch_cascade_t(const AttnParams& pre, const AttnParams& suf, hipStream_t stream) {
     const int pre_blocks = work_blocks(pre);   // a multiple of 8: every block keeps its XCD
     const int suf_blocks = work_blocks(suf);
-    // prefix row chunks of 32 rows (two row blocks) or 16 (one)
-    if ((pre.R + pre.row_chunks - 1) / pre.row_chunks > 16)
-        hipLaunchKernelGGL((attn_cascade_kernel<D, R, 2, QBF16, AFF>), dim3(pre_blocks + suf_blocks), dim3(256), 0,
-                           stream, pre, suf, pre_blocks);
-    else
-        hipLaunchKernelGGL((attn_cascade_kernel<D, R, 1, QBF16, AFF>), dim3(pre_blocks + suf_blocks), dim3(256), 0,
-                           stream, pre, suf, pre_blocks);
+    hipLaunchKernelGGL((attn_cascade_kernel<D, R, QBF16, AFF>), dim3(pre_blocks + suf_blocks), dim3(256), 0, stream,
+                       pre, suf, pre_blocks);
     return hipGetLastError();
 }
 
@@ -1263,8 +1255,7 @@ int32_t launch_dec2_append(const AttnParams& kp, const Plan& plan, int head_dim,
 // One launch of both cascade passes (prefix plan: 32-row blocks, 4 waves, 2
 // stages; suffix plan: replicated rows, 4 or 8 rows, 4 waves, 2 stages).
 bool cascade_fusable(const Plan& pre, const Plan& suf) {
-    return pre.kernel == kRows && pre.rows > 16 && (pre.rows_per_wg == 32 || pre.rows_per_wg == 16) &&
-           pre.waves == 4 && pre.stages == 2 &&
+    return pre.kernel == kRows && pre.rows_per_wg == 32 && pre.waves == 4 && pre.stages == 2 &&
            suf.kernel == kDec2 && (suf.rows == 4 || suf.rows == 8) && suf.waves == 4 && suf.stages == 2;
 }
 
