@@ -69,6 +69,26 @@ def test_many_sequences():
     assert np.all(got[5] == 0) and np.all(got[17] == 0)
 
 
+@pytest.mark.parametrize("hq,hkv,D,fp32", [(32, 8, 128, False), (2, 1, 64, True)])
+def test_every_sequence_empty(hq, hkv, D, fp32):
+    """Degenerate batch: every sequence is empty (max_seq_len 0).  The plan
+    has one split, no page is read, and every output row is written as zero
+    over an output buffer that starts as NaN."""
+    import torch
+
+    import decode_attention_quantized_kv_amd as q8
+    cache = q8.PagedKVCache(1, hkv, D)
+    q = torch.randn(3, hq, D, device="cuda")
+    if not fp32:
+        q = q.to(torch.bfloat16)
+    lens = torch.zeros(3, dtype=torch.int32, device="cuda")
+    table = torch.zeros(3, 1, dtype=torch.int32, device="cuda")
+    out = torch.full((3, hq, D), float("nan"), device="cuda")
+    q8.attn_decode_q8k4v(cache, q, lens, 0, table, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0), (hq, hkv, D)
+
+
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: "default" if c is None else "-".join(f"{k}{v}" for k, v in c.items()))
 def test_every_launch_configuration(cfg):
     from tests.gpu_util import run_attention, upload_cache
