@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -352,7 +351,7 @@ int32_t make_cascade_plan(const AttnArgs& a, int32_t n_pref, const q8k4v_config*
     const int64_t per = (int64_t)H * pp.row_chunks;
     // one prefix workgroup per CU on its own; one per two CUs in the fused
     // launch, which leaves room for the suffix workgroups (measured)
-    const int64_t target = fuse ? (getenv("Q8K4V_EXP_PRE1") ? device_cu_count() : device_cu_count() / 2) : device_cu_count();
+    const int64_t target = fuse ? device_cu_count() / 2 : device_cu_count();
     const int64_t splits = std::max<int64_t>(1, (target + per - 1) / per);
     int32_t spp = round_up((int32_t)((n_pref + splits - 1) / splits), unit);
     spp = std::min(std::max(spp, unit), 64 * pp.waves);
@@ -387,7 +386,7 @@ int32_t launch_cascade(const AttnArgs& a, int32_t n_pref, const CascadePlan& cp,
     pre.W = a.n_seqs;               // session j's rows are "draft" j
     pre.R = cp.pre.rows;
     pre.page_cap = n_pref;
-    pre.cascade = getenv("Q8K4V_EXP_PREPRIO") ? 2 : 1;
+    pre.cascade = 1;
     pre.direct = 0;
     pre.fused = 0;
 

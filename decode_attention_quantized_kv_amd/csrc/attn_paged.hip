@@ -1124,10 +1124,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(const AttnParams 
 template <int D, int R, bool QBF16, bool AFF>
 __global__ __launch_bounds__(256) void attn_cascade_kernel(const AttnParams pre, const AttnParams suf, int pre_blocks) {
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[4 * 2 * ring_stage_bytes<D, AFF>()];
-    if ((int)blockIdx.x < pre_blocks) {
-        if (pre.cascade == 2) __builtin_amdgcn_s_setprio(3);
-        rows_body<D, 2, 4, 2, QBF16, AFF>(pre, s_stage, (int)blockIdx.x);
-    }
+    if ((int)blockIdx.x < pre_blocks) rows_body<D, 2, 4, 2, QBF16, AFF>(pre, s_stage, (int)blockIdx.x);
     else dec2_body<D, R, 4, 2, QBF16, AFF>(suf, s_stage, (int)blockIdx.x - pre_blocks);
 }
 
