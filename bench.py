@@ -428,8 +428,8 @@ def run_probes(torch, q8, caches, seq_lens, msl, page_table, K, layers, cache_re
 # the summary is used only while these files are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    False: ["attn_paged.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp", "combine.hip"],
-    True: ["attn_paged.hip", "attn_common.h", "q8k4v_device.h", "abi.cpp", "combine.hip"],
+    False: ["attn_paged.hip", "attn_common.h", "q8k4v_device.h", "q8k4v_internal.h", "abi.cpp", "combine.hip"],
+    True: ["attn_paged.hip", "attn_common.h", "q8k4v_device.h", "q8k4v_internal.h", "abi.cpp", "combine.hip"],
 }
 
 

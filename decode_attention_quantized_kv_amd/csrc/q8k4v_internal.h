@@ -89,7 +89,7 @@ struct CascadePlan {
     Plan pre, suf;
 };
 constexpr int32_t kMaxPrefixRows = 4096;
-constexpr int32_t kCascadeSuffixWgsPerCu = 4;   // suffix pass, when the caller gives no config
+constexpr int32_t kCascadeSuffixWgsPerCu = 3;   // suffix pass, when the caller gives no config
 // Default suffix-pass configuration of the cascade for `group` query heads
 // per kv head (the decode defaults with kCascadeSuffixWgsPerCu).
 q8k4v_config cascade_default_config(int32_t group);

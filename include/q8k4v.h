@@ -229,7 +229,7 @@ int32_t attn_decode_q8k4v(const q8k4v_cache *cache, const void *q, int32_t q_dty
  *                   0 runs attn_decode_q8k4v.
  *   cfg             applies to the suffix pass (NULL: the configuration
  *                   tune_select installed for this device and head shape, else
- *                   the decode defaults with wgs_per_cu 4); the prefix pass
+ *                   the decode defaults with wgs_per_cu 3); the prefix pass
  *                   uses the row-block kernel's defaults
  *   workspace       at least q8k4v_prefix_workspace_bytes(...) bytes
  * Other arguments as attn_decode_q8k4v.  Errors as attn_decode_q8k4v, plus
