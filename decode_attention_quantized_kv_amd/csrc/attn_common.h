@@ -1,5 +1,5 @@
-// Pieces shared by the attention kernels (vector, 4x4x4 block MFMA, 16x16
-// MFMA, and the two tile-ring kernels of attn_paged.hip): launch parameters,
+// Pieces shared by the attention kernels (the replicated-row and row-block
+// tile-ring kernels of attn_paged.hip) and the combine kernels: launch parameters,
 // the XCD-aware work-item mapping, the merge of a workgroup's waves, the
 // split partials and the log-sum-exp combine of the splits (by the
 // last-arriving workgroup or by a separate kernel, and the two-source combine

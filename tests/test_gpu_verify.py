@@ -1,6 +1,6 @@
 """GPU parity of attn_verify_q8k4v against the fp64 oracle: draft widths
-and group sizes on every kernel (vector, 4x4x4 block MFMA, 16x16 MFMA), the
-causal rule among drafts (verify row j equals a decode at length L-W+j+1),
+and group sizes on both kernels (the replicated-row kernel for 1, 2, 4, 8 or
+16 rows per kv head, the row-block kernel otherwise), the causal rule among drafts (verify row j equals a decode at length L-W+j+1),
 ragged batches, and the full 64K verify workload."""
 
 import numpy as np
